@@ -1,0 +1,225 @@
+/*
+ * libmuon — one Muon optimizer step on an AMD Instinct MI355X (gfx950).
+ *
+ * The step the pages describe ("Frontier Pre-training at Microsoft AI", method details
+ * section 5, "Scaling Muon to 16K GPUs", resharding steps 1, 3 and 5; the same step in
+ * "Microsoft Reveals MAI-Base-2 Training Recipe ...", section "How to Make Parameter
+ * Updates Faster and More Stable?"):
+ *
+ *   1. each GPU updates its FP32 momentum and casts it to BF16;
+ *   3. each GPU orthogonalises whole momentum matrices, batched by shape, with a
+ *      Newton–Schulz operator built for the symmetric intermediates;
+ *   5. the update is cast back to FP32 and applied to the weights.
+ *
+ * On one GPU the all-to-all exchanges of steps 2 and 4 have no counterpart: this library
+ * takes one GPU's share of whole matrices.  The shape batching and the cached metadata
+ * of that section ("parameter matrices of the same shape are packed into a batch";
+ * "resharding index metadata is computed once and cached") become the plan below.
+ *
+ * Memory and ownership
+ *   The caller owns every device buffer: weights W, momenta M, gradients G and the
+ *   workspace.  The library owns only the host-side plan object.  It never allocates or
+ *   frees device memory.  All step calls are asynchronous on the given stream, never
+ *   synchronise, and can be captured in a HIP graph.
+ *
+ * Errors
+ *   Every call returns a muon_status synchronously; MUON_OK is 0.  muon_last_error()
+ *   gives a message for the last failing call on the calling thread.  Device faults
+ *   surface at the caller's next synchronisation.  NaN and Inf are data, not errors:
+ *   they stay inside the matrix they occur in.
+ *
+ * Threading
+ *   A bound plan's layout never changes.  Step calls on one plan must not overlap on
+ *   different streams: they share the workspace.
+ *
+ * Streams are passed as `void*` holding a hipStream_t (NULL = the null stream).
+ */
+#ifndef LIBMUON_MUON_H
+#define LIBMUON_MUON_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MUON_API __attribute__((visibility("default")))
+#else
+#define MUON_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t muon_status;
+#define MUON_OK 0
+#define MUON_ERR_INVALID_ARG 1         /* null pointer, bad enum, bad chunk or scalar     */
+#define MUON_ERR_SHAPE 2               /* zero or oversized dimension                     */
+#define MUON_ERR_ALIGNMENT 3           /* device pointer not 16-byte aligned              */
+#define MUON_ERR_WORKSPACE_TOO_SMALL 4 /* workspace below muon_plan_workspace_bytes()     */
+#define MUON_ERR_NOT_BOUND 5           /* step call before muon_plan_bind()               */
+#define MUON_ERR_STALE_PLAN 6          /* descriptors no longer match the plan            */
+#define MUON_ERR_HIP 7                 /* a HIP runtime call failed (message in last_error) */
+
+#define MUON_DTYPE_F32 0
+#define MUON_DTYPE_BF16 1
+
+/* One parameter as the caller holds it.  Only ndim == 2 parameters take the Muon step
+ * (the pages apply Muon to every 2-D non-embedding matrix and AdamW to the rest —
+ * "Frontier Pre-training at Microsoft AI", setup section 4); any other ndim is counted
+ * as excluded and its pointers are not read.
+ * weight, momentum: device, rows x cols float32, row-major, contiguous, 16-B aligned.
+ * grad: device, rows x cols of grad_dtype, row-major, contiguous, 16-B aligned.
+ * weight and momentum must not overlap each other, any other parameter's, or a grad. */
+typedef struct muon_param_desc {
+    int32_t ndim;
+    int32_t grad_dtype; /* MUON_DTYPE_F32 or MUON_DTYPE_BF16 */
+    int64_t rows;
+    int64_t cols;
+    float* weight;
+    float* momentum;
+    const void* grad;
+} muon_param_desc;
+
+/* Plan options.  A zero-filled struct (or NULL) means: no workspace cap, scale 1. */
+typedef struct muon_plan_opts {
+    /* Upper bound on the workspace in bytes; 0 = no bound.  Above the bound, buckets
+     * are split into chunks that share one workspace region and must then be stepped
+     * one chunk at a time (momentum, NS, apply for chunk i before chunk i+1). */
+    uint64_t max_workspace_bytes;
+    /* Host, nullable: per-parameter update scale s_i (n entries, indexed like the
+     * descriptors; entries of excluded parameters are ignored).  NULL means s_i = 1.
+     * The pages give no scale rule; the scale is a free per-matrix factor. */
+    const float* scale;
+} muon_plan_opts;
+
+typedef struct muon_plan muon_plan;
+
+/* Per-chunk facts, for reporting. */
+typedef struct muon_chunk_info {
+    int64_t m, n;          /* canonical shape: m = min(rows, cols), n = max(rows, cols) */
+    int64_t m_pad, n_pad;  /* padded workspace shape of every matrix in the chunk       */
+    int64_t count;         /* matrices in the chunk                                    */
+    int32_t bucket;        /* bucket id (chunks of one bucket share it)                */
+    int32_t tile;          /* Newton–Schulz output tile edge                           */
+    int32_t grad_dtype;
+    int32_t shared_region; /* 1 when this chunk shares its workspace region            */
+    double flops_conventional; /* per NS iteration: 4 m^2 n + 2 m^3, times count        */
+    double flops_algorithmic;  /* per NS iteration: m(m+1)n + m^2(m+1) + 2 m^2 n, x count */
+    double bytes_momentum;     /* algorithmic HBM bytes of the momentum kernel          */
+    double bytes_apply;        /* algorithmic HBM bytes of the apply kernel             */
+    uint64_t region_offset;    /* byte offset of the chunk's region in the workspace    */
+    uint64_t region_bytes;
+} muon_chunk_info;
+
+/* Where one parameter's orthogonalised update O lives after muon_ns_batched. */
+typedef struct muon_param_info {
+    int32_t included;       /* 0 for excluded (ndim != 2) parameters; rest is then 0  */
+    int32_t chunk;
+    int64_t slot;           /* index of the matrix inside its chunk                   */
+    int32_t transposed;     /* 1 when rows > cols: O is stored as the m x n transpose */
+    int32_t reserved;
+    uint64_t output_offset; /* byte offset of O (bf16, m x n, row stride ld) in the workspace */
+    int64_t ld;             /* row stride of O in elements (= n_pad)                  */
+} muon_param_info;
+
+/* ---- plan (host only; no device calls) ---------------------------------------------- */
+
+/* Build a plan for n parameters: exclude ndim != 2, canonicalise each matrix to
+ * (m, n) = (min, max) with a transpose flag when rows > cols, group by (m, n, grad
+ * dtype) into buckets, split buckets into chunks under the workspace cap, lay out the
+ * workspace and build the per-matrix tables.  On success *out owns a new plan.
+ * Errors: INVALID_ARG (null params with n > 0, null out, bad dtype, null or
+ * overlapping buffers), SHAPE (rows or cols <= 0, or a padded matrix above 2^31
+ * elements), ALIGNMENT (a buffer not 16-B aligned), WORKSPACE_TOO_SMALL (one matrix of
+ * some bucket does not fit under the cap). */
+MUON_API muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
+                              const muon_plan_opts* opts, muon_plan** out);
+
+/* Bytes of device workspace the plan needs (256-B aligned start required). */
+MUON_API muon_status muon_plan_workspace_bytes(const muon_plan* plan, uint64_t* bytes);
+
+/* Number of chunks; counts of included and excluded parameters (any pointer may be NULL). */
+MUON_API muon_status muon_plan_counts(const muon_plan* plan, int32_t* n_chunks, int32_t* n_buckets,
+                             int64_t* n_included, int64_t* n_excluded);
+
+MUON_API muon_status muon_plan_info(const muon_plan* plan, int32_t chunk, muon_chunk_info* out);
+
+MUON_API muon_status muon_plan_param_info(const muon_plan* plan, int64_t param, muon_param_info* out);
+
+/* STALE_PLAN when the descriptors differ from those the plan was built from (count,
+ * ndim, shape, dtype or any pointer), else OK. */
+MUON_API muon_status muon_plan_validate(const muon_plan* plan, const muon_param_desc* params, int64_t n);
+
+/* ---- bind (device) ------------------------------------------------------------------- */
+
+/* Attach a caller-owned device workspace (>= muon_plan_workspace_bytes, 256-B aligned)
+ * and upload the plan's tables, ordered on `stream`.  Also zero-fills the workspace.
+ * May be called again with another workspace. */
+MUON_API muon_status muon_plan_bind(muon_plan* plan, void* workspace, uint64_t bytes, void* stream);
+
+/* ---- the step (device, asynchronous on `stream`) --------------------------------------- */
+
+/* Step 1.  For every matrix of `chunk` (-1 = every chunk; not allowed when chunks share
+ * a region): M <- beta*M + (1-beta)*G with both products and the sum in float64 and one
+ * float32 store; X0 = bf16(M) (round to nearest even) written to the workspace in
+ * canonical orientation; per-tile sums of X0^2 for the normaliser.  beta = 0 copies G
+ * into M.  Errors: INVALID_ARG (chunk, non-finite beta), NOT_BOUND, HIP. */
+MUON_API muon_status muon_momentum_update(const muon_plan* plan, int32_t chunk, float beta, void* stream);
+
+/* Step 3.  For every matrix of `chunk`: X = bf16(X0 / (||X0||_F + eps)), then `steps`
+ * quintic Newton–Schulz iterations, each
+ *     A = X X^T (bf16),  B = b A + c A A (bf16),  X = a X + B X (bf16),
+ * with bf16 MFMA products accumulated in float32.  A and B are symmetric; only their
+ * upper-triangle tiles are computed and then mirrored.  The result O is left in the
+ * workspace (see muon_plan_param_info).  The pages give no coefficients or step count;
+ * (3.4445, -4.7750, 2.0315), 5 steps and eps = 1e-7 are the usual choice.
+ * Errors: INVALID_ARG (chunk, steps < 1, non-finite scalars), NOT_BOUND, HIP. */
+MUON_API muon_status muon_ns_batched(const muon_plan* plan, int32_t chunk, float a, float b, float c,
+                            int32_t steps, float eps, void* stream);
+
+/* Step 5.  For every matrix of `chunk`: W <- f32((1 - lr*wd) * W - lr*s_i*O), each
+ * product and the difference rounded to float64 separately (no fused multiply-add),
+ * O read back in the parameter's own orientation.  Decoupled weight decay: the decay's
+ * time scale is 1/(lr*wd) ("Frontier Pre-training at Microsoft AI", method details
+ * section 3), so lr and wd are plain arguments and wd = 17.04/(steps*lr) plugs in.
+ * Errors: INVALID_ARG (chunk, non-finite lr or wd), NOT_BOUND, HIP. */
+MUON_API muon_status muon_apply(const muon_plan* plan, int32_t chunk, float lr, float wd, void* stream);
+
+/* Steps 1, 3 and 5 for `chunk` (-1 = every chunk, in order), with the arguments above. */
+MUON_API muon_status muon_step(const muon_plan* plan, int32_t chunk, float beta, float a, float b,
+                      float c, int32_t steps, float eps, float lr, float wd, void* stream);
+
+/* ---- per-kernel timing (HIP events on the launching stream) --------------------------- */
+
+#define MUON_KERNEL_MOMENTUM 0
+#define MUON_KERNEL_NORM_FINALIZE 1
+#define MUON_KERNEL_NORMALIZE 2
+#define MUON_KERNEL_SYRK 3
+#define MUON_KERNEL_SYRK_POLY 4
+#define MUON_KERNEL_GEMM_AXPY 5
+#define MUON_KERNEL_APPLY 6
+#define MUON_KERNEL_COUNT 7
+
+/* Start recording a HIP event pair around every kernel launch of this plan (up to
+ * `capacity` launches; later ones go unrecorded).  capacity = 0 stops recording.
+ * Not for use while a graph is being captured. */
+MUON_API muon_status muon_timing_enable(muon_plan* plan, int32_t capacity);
+/* Wait for the recorded events and return, for one kernel kind, the summed duration
+ * in milliseconds, the launch count and the summed algorithmic work of those launches
+ * (FLOPs for the Newton–Schulz kernels, HBM bytes for the others).  Clears nothing. */
+MUON_API muon_status muon_timing_read(muon_plan* plan, int32_t kernel, double* total_ms,
+                             int64_t* launches, double* work);
+/* Forget recorded launches (events are kept for reuse). */
+MUON_API muon_status muon_timing_reset(muon_plan* plan);
+MUON_API const char* muon_kernel_name(int32_t kernel);
+
+/* ---- teardown and errors ------------------------------------------------------------ */
+
+MUON_API void muon_plan_destroy(muon_plan* plan);
+MUON_API const char* muon_status_string(muon_status status);
+MUON_API const char* muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMUON_MUON_H */

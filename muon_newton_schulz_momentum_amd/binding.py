@@ -1,0 +1,128 @@
+"""ctypes binding of libmuon.so (include/muon.h): the same names, argument marshalling only.
+
+Importing this module loads the in-tree libmuon.so and raises if it is missing; there is
+no fallback path of any kind.  Build it with `python -m muon_newton_schulz_momentum_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libmuon.so is not built ({LIB_PATH} missing); run "
+                      "`python -m muon_newton_schulz_momentum_amd.build` first")
+
+# torch ships its own HIP runtime, loaded under the file name libamdhip64.so.  libmuon.so
+# asks for libamdhip64.so.7; if it is loaded first, the process ends up with two HIP
+# runtimes and the second finds no device.  Importing torch first makes libmuon bind to
+# torch's already-loaded runtime (same soname), so both share one device context.
+import torch  # noqa: E402,F401
+
+_lib = C.CDLL(LIB_PATH)
+
+# ---- constants (include/muon.h) ----------------------------------------------------------
+MUON_OK = 0
+MUON_ERR_INVALID_ARG = 1
+MUON_ERR_SHAPE = 2
+MUON_ERR_ALIGNMENT = 3
+MUON_ERR_WORKSPACE_TOO_SMALL = 4
+MUON_ERR_NOT_BOUND = 5
+MUON_ERR_STALE_PLAN = 6
+MUON_ERR_HIP = 7
+
+MUON_DTYPE_F32 = 0
+MUON_DTYPE_BF16 = 1
+
+MUON_KERNEL_MOMENTUM = 0
+MUON_KERNEL_NORM_FINALIZE = 1
+MUON_KERNEL_NORMALIZE = 2
+MUON_KERNEL_SYRK = 3
+MUON_KERNEL_SYRK_POLY = 4
+MUON_KERNEL_GEMM_AXPY = 5
+MUON_KERNEL_APPLY = 6
+MUON_KERNEL_COUNT = 7
+
+
+class muon_param_desc(C.Structure):
+    _fields_ = [("ndim", C.c_int32), ("grad_dtype", C.c_int32), ("rows", C.c_int64),
+                ("cols", C.c_int64), ("weight", C.c_void_p), ("momentum", C.c_void_p),
+                ("grad", C.c_void_p)]
+
+
+class muon_plan_opts(C.Structure):
+    _fields_ = [("max_workspace_bytes", C.c_uint64), ("scale", C.POINTER(C.c_float))]
+
+
+class muon_chunk_info(C.Structure):
+    _fields_ = [("m", C.c_int64), ("n", C.c_int64), ("m_pad", C.c_int64), ("n_pad", C.c_int64),
+                ("count", C.c_int64), ("bucket", C.c_int32), ("tile", C.c_int32),
+                ("grad_dtype", C.c_int32), ("shared_region", C.c_int32),
+                ("flops_conventional", C.c_double), ("flops_algorithmic", C.c_double),
+                ("bytes_momentum", C.c_double), ("bytes_apply", C.c_double),
+                ("region_offset", C.c_uint64), ("region_bytes", C.c_uint64)]
+
+
+class muon_param_info(C.Structure):
+    _fields_ = [("included", C.c_int32), ("chunk", C.c_int32), ("slot", C.c_int64),
+                ("transposed", C.c_int32), ("reserved", C.c_int32),
+                ("output_offset", C.c_uint64), ("ld", C.c_int64)]
+
+
+_P = C.c_void_p  # muon_plan*
+
+
+def _fn(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+muon_plan_buckets = _fn("muon_plan_buckets", C.c_int32,
+                        [C.POINTER(muon_param_desc), C.c_int64, C.POINTER(muon_plan_opts), C.POINTER(_P)])
+muon_plan_workspace_bytes = _fn("muon_plan_workspace_bytes", C.c_int32, [_P, C.POINTER(C.c_uint64)])
+muon_plan_counts = _fn("muon_plan_counts", C.c_int32,
+                       [_P, C.POINTER(C.c_int32), C.POINTER(C.c_int32), C.POINTER(C.c_int64),
+                        C.POINTER(C.c_int64)])
+muon_plan_info = _fn("muon_plan_info", C.c_int32, [_P, C.c_int32, C.POINTER(muon_chunk_info)])
+muon_plan_param_info = _fn("muon_plan_param_info", C.c_int32, [_P, C.c_int64, C.POINTER(muon_param_info)])
+muon_plan_validate = _fn("muon_plan_validate", C.c_int32, [_P, C.POINTER(muon_param_desc), C.c_int64])
+muon_plan_bind = _fn("muon_plan_bind", C.c_int32, [_P, C.c_void_p, C.c_uint64, C.c_void_p])
+muon_momentum_update = _fn("muon_momentum_update", C.c_int32, [_P, C.c_int32, C.c_float, C.c_void_p])
+muon_ns_batched = _fn("muon_ns_batched", C.c_int32,
+                      [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float, C.c_void_p])
+muon_apply = _fn("muon_apply", C.c_int32, [_P, C.c_int32, C.c_float, C.c_float, C.c_void_p])
+muon_step = _fn("muon_step", C.c_int32,
+                [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float,
+                 C.c_float, C.c_float, C.c_void_p])
+muon_timing_enable = _fn("muon_timing_enable", C.c_int32, [_P, C.c_int32])
+muon_timing_read = _fn("muon_timing_read", C.c_int32,
+                       [_P, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)])
+muon_timing_reset = _fn("muon_timing_reset", C.c_int32, [_P])
+muon_kernel_name = _fn("muon_kernel_name", C.c_char_p, [C.c_int32])
+muon_plan_destroy = _fn("muon_plan_destroy", None, [_P])
+muon_status_string = _fn("muon_status_string", C.c_char_p, [C.c_int32])
+muon_last_error = _fn("muon_last_error", C.c_char_p, [])
+
+EXPORTED = [
+    "muon_plan_buckets", "muon_plan_workspace_bytes", "muon_plan_counts", "muon_plan_info",
+    "muon_plan_param_info", "muon_plan_validate", "muon_plan_bind", "muon_momentum_update",
+    "muon_ns_batched", "muon_apply", "muon_step", "muon_timing_enable", "muon_timing_read",
+    "muon_timing_reset", "muon_kernel_name", "muon_plan_destroy", "muon_status_string",
+    "muon_last_error",
+]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = muon_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {muon_status_string(status).decode()} ({status}): {msg}")
+
+
+def check(status: int, where: str) -> None:
+    if status != MUON_OK:
+        raise MuonError(status, where)

@@ -1,0 +1,344 @@
+// Device-side entry points of libmuon: bind, the three step calls, and kernel timing.
+// Argument checks happen here, on the host, before anything is launched; a kernel is
+// only launched with shapes the planner has laid out in the workspace.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <string>
+
+#include "kernels.h"
+#include "plan_internal.h"
+
+using namespace muon;
+
+namespace {
+
+muon_status hip_fail(hipError_t e, const char* what) {
+    return set_error(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <class T>
+T* at(const muon_plan* p, uint64_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(p->ws) + off);
+}
+
+muon_status check_step(const muon_plan* p, int32_t chunk, const char* who) {
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": plan is NULL");
+    if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, std::string(who) + ": call muon_plan_bind first");
+    if (chunk < -1 || chunk >= (int32_t)p->chunks.size())
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": chunk out of range");
+    if (chunk == -1 && p->shared_regions && p->chunks.size() > 1)
+        return set_error(MUON_ERR_INVALID_ARG,
+                         std::string(who) + ": the chunks share one workspace region; "
+                                            "step them one at a time (or use muon_step)");
+    return MUON_OK;
+}
+
+// ---- per-launch timing ------------------------------------------------------------------
+
+struct TimedLaunch {
+    muon_plan* p;
+    int slot = -1;
+    TimedLaunch(const muon_plan* plan, int32_t kind, double work, hipStream_t s)
+        : p(const_cast<muon_plan*>(plan)) {
+        TimingState& t = p->timing;
+        if (t.used >= t.capacity) return;
+        slot = t.used++;
+        t.kind[slot] = kind;
+        t.work[slot] = work;
+        (void)hipEventRecord((hipEvent_t)t.ev_begin[slot], s);
+    }
+    void done(hipStream_t s) {
+        if (slot >= 0) (void)hipEventRecord((hipEvent_t)p->timing.ev_end[slot], s);
+    }
+};
+
+// ---- the three steps for one chunk --------------------------------------------------------
+
+muon_status momentum_chunk(const muon_plan* p, const Chunk& c, float beta, hipStream_t s) {
+    MomentumArgs a;
+    a.tbl = at<const MatEntry>(p, c.off_table);
+    a.xq = at<uint16_t>(p, c.off_xq);
+    a.partials = at<double>(p, c.off_part);
+    a.mat_stride = c.mp * c.np;
+    a.np = c.np;
+    a.ew_tiles = c.ew_tiles;
+    a.total_tiles = c.count * c.ew_tiles;
+    a.beta = beta;
+    a.omb = 1.0f - beta;
+    const double gsz = c.grad_dtype == MUON_DTYPE_F32 ? 4.0 : 2.0;
+    TimedLaunch tl(p, MUON_KERNEL_MOMENTUM, (double)c.count * c.m * c.n * (10.0 + gsz), s);
+    const hipError_t e = launch_momentum(a, c.grad_dtype, s);
+    tl.done(s);
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "momentum kernel launch");
+}
+
+muon_status ns_chunk(const muon_plan* p, const Chunk& c, float a_, float b_, float c_, int32_t steps,
+                     float eps, hipStream_t s) {
+    uint16_t* xp = at<uint16_t>(p, c.off_xp);
+    uint16_t* xq = at<uint16_t>(p, c.off_xq);
+    uint16_t* am = at<uint16_t>(p, c.off_a);
+    uint16_t* bm = at<uint16_t>(p, c.off_b);
+    double* inv = at<double>(p, c.off_inv);
+    hipError_t e;
+
+    {
+        FinalizeArgs f{at<const double>(p, c.off_part), inv, c.ew_tiles, (double)eps};
+        TimedLaunch tl(p, MUON_KERNEL_NORM_FINALIZE, (double)c.count * c.ew_tiles * 8.0, s);
+        e = launch_finalize(f, c.count, s);
+        tl.done(s);
+        if (e != hipSuccess) return hip_fail(e, "norm finalize kernel launch");
+    }
+    // The iteration ping-pongs between the two X buffers and must end in xp, where the
+    // apply step reads O: start in xq (normalised in place) for an odd step count.
+    uint16_t* cur = (steps & 1) ? xq : xp;
+    {
+        NormalizeArgs n{xq, cur, inv, c.m, c.n, c.mp, c.np, c.count * c.mp * c.np / 8};
+        TimedLaunch tl(p, MUON_KERNEL_NORMALIZE, (double)c.count * c.m * c.n * 4.0, s);
+        e = launch_normalize(n, s);
+        tl.done(s);
+        if (e != hipSuccess) return hip_fail(e, "normalize kernel launch");
+    }
+
+    const int32_t tile = c.tile;
+    const int32_t tm = (int32_t)(c.mp / tile), tn = (int32_t)(c.np / tile);
+    const int32_t tri = tm * (tm + 1) / 2;
+    const int64_t xs = c.mp * c.np, as = c.mp * c.mp;
+    const double m = (double)c.m, n = (double)c.n, cnt = (double)c.count;
+
+    for (int32_t it = 0; it < steps; ++it) {
+        uint16_t* nxt = (cur == xp) ? xq : xp;
+        NsArgs g{};
+        // A = X X^T
+        g.opa = cur; g.opb = cur; g.ep = cur; g.out = am;
+        g.stride_a = xs; g.stride_b = xs; g.stride_o = as;
+        g.lda = (int32_t)c.np; g.ldb = (int32_t)c.np; g.ldo = (int32_t)c.mp;
+        g.K = (int32_t)c.np; g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tri;
+        g.total_tiles = (int32_t)(c.count * tri); g.alpha = 0.f; g.gamma = 1.f;
+        {
+            TimedLaunch tl(p, MUON_KERNEL_SYRK, cnt * m * (m + 1.0) * n, s);
+            e = launch_ns(NS_SYRK, tile, g, s);
+            tl.done(s);
+            if (e != hipSuccess) return hip_fail(e, "SYRK kernel launch");
+        }
+        // B = b A + c A A^T
+        g.opa = am; g.opb = am; g.ep = am; g.out = bm;
+        g.stride_a = as; g.stride_b = as; g.stride_o = as;
+        g.lda = (int32_t)c.mp; g.ldb = (int32_t)c.mp; g.ldo = (int32_t)c.mp;
+        g.K = (int32_t)c.mp; g.alpha = b_; g.gamma = c_;
+        {
+            TimedLaunch tl(p, MUON_KERNEL_SYRK_POLY, cnt * m * m * (m + 1.0), s);
+            e = launch_ns(NS_POLY, tile, g, s);
+            tl.done(s);
+            if (e != hipSuccess) return hip_fail(e, "SYRK+poly kernel launch");
+        }
+        // X' = a X + B X
+        g.opa = bm; g.opb = cur; g.ep = cur; g.out = nxt;
+        g.stride_a = as; g.stride_b = xs; g.stride_o = xs;
+        g.lda = (int32_t)c.mp; g.ldb = (int32_t)c.np; g.ldo = (int32_t)c.np;
+        g.K = (int32_t)c.mp; g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn;
+        g.total_tiles = (int32_t)(c.count * tm * tn); g.alpha = a_; g.gamma = 1.f;
+        {
+            TimedLaunch tl(p, MUON_KERNEL_GEMM_AXPY, cnt * 2.0 * m * m * n, s);
+            e = launch_ns(NS_AXPY, tile, g, s);
+            tl.done(s);
+            if (e != hipSuccess) return hip_fail(e, "GEMM+axpy kernel launch");
+        }
+        cur = nxt;
+    }
+    return MUON_OK;
+}
+
+muon_status apply_chunk(const muon_plan* p, const Chunk& c, float lr, float wd, hipStream_t s) {
+    ApplyArgs a;
+    a.tbl = at<const MatEntry>(p, c.off_table);
+    a.xo = at<const uint16_t>(p, c.off_xp);
+    a.mat_stride = c.mp * c.np;
+    a.np = c.np;
+    a.ew_tiles = c.ew_tiles;
+    a.total_tiles = c.count * c.ew_tiles;
+    const double lw = (double)lr * (double)wd;   // exact
+    a.d = 1.0 - lw;                               // one float64 rounding
+    a.lr = lr;
+    TimedLaunch tl(p, MUON_KERNEL_APPLY, (double)c.count * c.m * c.n * 10.0, s);
+    const hipError_t e = launch_apply(a, s);
+    tl.done(s);
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "apply kernel launch");
+}
+
+bool finite(float v) { return std::isfinite(v); }
+
+// The tile grid of a chunk must fit the kernels' int32 indexing.
+bool grid_fits(const Chunk& c) {
+    const int64_t tm = c.mp / c.tile, tn = c.np / c.tile;
+    return c.count * tm * tn < (int64_t(1) << 31) && c.count * tm * (tm + 1) / 2 < (int64_t(1) << 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_internal_release(muon_plan* p) {
+    for (void* ev : p->timing.ev_begin) (void)hipEventDestroy((hipEvent_t)ev);
+    for (void* ev : p->timing.ev_end) (void)hipEventDestroy((hipEvent_t)ev);
+    p->timing = TimingState{};
+}
+
+muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream) {
+    clear_error();
+    if (!p || !ws) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_bind: NULL plan or workspace");
+    if (((uintptr_t)ws & (WS_ALIGN - 1)) != 0)
+        return set_error(MUON_ERR_ALIGNMENT, "muon_plan_bind: workspace must be 256-byte aligned");
+    if (bytes < p->ws_bytes)
+        return set_error(MUON_ERR_WORKSPACE_TOO_SMALL, "muon_plan_bind: workspace holds " + std::to_string(bytes) +
+                                                           " bytes; the plan needs " + std::to_string(p->ws_bytes));
+    for (const Chunk& c : p->chunks)
+        if (!grid_fits(c)) return set_error(MUON_ERR_SHAPE, "muon_plan_bind: chunk tile grid exceeds 2^31 tiles");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemsetAsync(ws, 0, p->ws_bytes, s);
+    if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipMemsetAsync");
+    if (!p->table.empty()) {
+        e = hipMemcpyAsync(ws, p->table.data(), p->table.size() * sizeof(MatEntry), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: table upload");
+        // the host table is pageable memory owned by the plan; make sure the copy has
+        // consumed it before the caller can free or change anything
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: stream synchronize");
+    }
+    p->ws = ws;
+    p->ws_given = bytes;
+    p->bound = true;
+    return MUON_OK;
+}
+
+muon_status muon_momentum_update(const muon_plan* p, int32_t chunk, float beta, void* stream) {
+    clear_error();
+    muon_status st = check_step(p, chunk, "muon_momentum_update");
+    if (st != MUON_OK) return st;
+    if (!finite(beta)) return set_error(MUON_ERR_INVALID_ARG, "muon_momentum_update: beta must be finite");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        if (chunk != -1 && i != chunk) continue;
+        if ((st = momentum_chunk(p, p->chunks[(size_t)i], beta, s)) != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
+muon_status muon_ns_batched(const muon_plan* p, int32_t chunk, float a, float b, float c, int32_t steps,
+                            float eps, void* stream) {
+    clear_error();
+    muon_status st = check_step(p, chunk, "muon_ns_batched");
+    if (st != MUON_OK) return st;
+    if (steps < 1) return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched: steps must be >= 1");
+    if (!finite(a) || !finite(b) || !finite(c) || !finite(eps) || eps < 0.f)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched: coefficients must be finite and eps >= 0");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        if (chunk != -1 && i != chunk) continue;
+        if ((st = ns_chunk(p, p->chunks[(size_t)i], a, b, c, steps, eps, s)) != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
+muon_status muon_apply(const muon_plan* p, int32_t chunk, float lr, float wd, void* stream) {
+    clear_error();
+    muon_status st = check_step(p, chunk, "muon_apply");
+    if (st != MUON_OK) return st;
+    if (!finite(lr) || !finite(wd)) return set_error(MUON_ERR_INVALID_ARG, "muon_apply: lr and wd must be finite");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        if (chunk != -1 && i != chunk) continue;
+        if ((st = apply_chunk(p, p->chunks[(size_t)i], lr, wd, s)) != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
+muon_status muon_step(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,
+                      float eps, float lr, float wd, void* stream) {
+    clear_error();
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_step: plan is NULL");
+    if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_step: call muon_plan_bind first");
+    if (chunk < -1 || chunk >= (int32_t)p->chunks.size())
+        return set_error(MUON_ERR_INVALID_ARG, "muon_step: chunk out of range");
+    if (!finite(beta) || !finite(lr) || !finite(wd) || !finite(a) || !finite(b) || !finite(c) || !finite(eps) ||
+        eps < 0.f || steps < 1)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_step: scalars must be finite, eps >= 0 and steps >= 1");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    muon_status st;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        if (chunk != -1 && i != chunk) continue;
+        const Chunk& ch = p->chunks[(size_t)i];
+        if ((st = momentum_chunk(p, ch, beta, s)) != MUON_OK) return st;
+        if ((st = ns_chunk(p, ch, a, b, c, steps, eps, s)) != MUON_OK) return st;
+        if ((st = apply_chunk(p, ch, lr, wd, s)) != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
+muon_status muon_timing_enable(muon_plan* p, int32_t capacity) {
+    clear_error();
+    if (!p || capacity < 0) return set_error(MUON_ERR_INVALID_ARG, "muon_timing_enable: bad argument");
+    TimingState& t = p->timing;
+    while ((int32_t)t.ev_begin.size() < capacity) {
+        hipEvent_t b0, e0;
+        hipError_t e = hipEventCreate(&b0);
+        if (e != hipSuccess) return hip_fail(e, "muon_timing_enable: hipEventCreate");
+        e = hipEventCreate(&e0);
+        if (e != hipSuccess) {
+            (void)hipEventDestroy(b0);
+            return hip_fail(e, "muon_timing_enable: hipEventCreate");
+        }
+        t.ev_begin.push_back(b0);
+        t.ev_end.push_back(e0);
+    }
+    t.kind.assign((size_t)capacity, -1);
+    t.work.assign((size_t)capacity, 0.0);
+    t.capacity = capacity;
+    t.used = 0;
+    return MUON_OK;
+}
+
+muon_status muon_timing_reset(muon_plan* p) {
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_timing_reset: plan is NULL");
+    p->timing.used = 0;
+    return MUON_OK;
+}
+
+muon_status muon_timing_read(muon_plan* p, int32_t kernel, double* total_ms, int64_t* launches, double* work) {
+    clear_error();
+    if (!p || kernel < 0 || kernel >= MUON_KERNEL_COUNT)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_timing_read: bad argument");
+    double ms = 0.0, wk = 0.0;
+    int64_t n = 0;
+    TimingState& t = p->timing;
+    for (int32_t i = 0; i < t.used; ++i) {
+        if (t.kind[(size_t)i] != kernel) continue;
+        hipError_t e = hipEventSynchronize((hipEvent_t)t.ev_end[(size_t)i]);
+        if (e != hipSuccess) return hip_fail(e, "muon_timing_read: hipEventSynchronize");
+        float f = 0.f;
+        e = hipEventElapsedTime(&f, (hipEvent_t)t.ev_begin[(size_t)i], (hipEvent_t)t.ev_end[(size_t)i]);
+        if (e != hipSuccess) return hip_fail(e, "muon_timing_read: hipEventElapsedTime");
+        ms += f;
+        wk += t.work[(size_t)i];
+        ++n;
+    }
+    if (total_ms) *total_ms = ms;
+    if (launches) *launches = n;
+    if (work) *work = wk;
+    return MUON_OK;
+}
+
+const char* muon_kernel_name(int32_t k) {
+    switch (k) {
+        case MUON_KERNEL_MOMENTUM: return "momentum";
+        case MUON_KERNEL_NORM_FINALIZE: return "norm_finalize";
+        case MUON_KERNEL_NORMALIZE: return "normalize";
+        case MUON_KERNEL_SYRK: return "syrk";
+        case MUON_KERNEL_SYRK_POLY: return "syrk_poly";
+        case MUON_KERNEL_GEMM_AXPY: return "gemm_axpy";
+        case MUON_KERNEL_APPLY: return "apply";
+        default: return "unknown";
+    }
+}
+
+}  // extern "C"

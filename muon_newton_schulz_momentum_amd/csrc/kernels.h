@@ -1,0 +1,75 @@
+// Launch wrappers for the libmuon kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan_internal.h"
+
+namespace muon {
+
+struct MomentumArgs {
+    const MatEntry* tbl;   // the chunk's table rows (device)
+    uint16_t* xq;          // X0 destination: count matrices of mp x np bf16
+    double* partials;      // count * ew_tiles sums of squares
+    int64_t mat_stride;    // mp * np
+    int64_t np;
+    int64_t ew_tiles;
+    int64_t total_tiles;   // count * ew_tiles
+    float beta, omb;       // beta and (1 - beta), both as the caller's float32
+};
+
+struct FinalizeArgs {
+    const double* partials;
+    double* inv;           // per matrix: 1 / (sqrt(sum) + eps)
+    int64_t ew_tiles;
+    double eps;
+};
+
+struct NormalizeArgs {
+    const uint16_t* src;   // X0 (valid m x n region, row stride np)
+    uint16_t* dst;         // X, whole mp x np region (pads zeroed); may equal src
+    const double* inv;
+    int64_t m, n, mp, np;
+    int64_t total_units;   // count * mp * np / 8
+};
+
+struct ApplyArgs {
+    const MatEntry* tbl;
+    const uint16_t* xo;    // O: count matrices of mp x np bf16 (canonical orientation)
+    int64_t mat_stride;
+    int64_t np;
+    int64_t ew_tiles;
+    int64_t total_tiles;
+    double d;              // 1 - lr*wd, formed in float64
+    float lr;
+};
+
+// Newton–Schulz GEMM kernels.  opa/opb are matrix-0 bases; every matrix of the chunk
+// sits `stride_*` elements after the previous one.
+enum NsMode : int32_t { NS_SYRK = 0, NS_POLY = 1, NS_AXPY = 2 };
+
+struct NsArgs {
+    const uint16_t* opa;   // SYRK: X; POLY: A; AXPY: B   (row panels, K contiguous)
+    const uint16_t* opb;   // SYRK: X; POLY: A; AXPY: X   (AXPY: K x N, N contiguous)
+    const uint16_t* ep;    // epilogue input: POLY: A; AXPY: X; SYRK: unused
+    uint16_t* out;         // SYRK: A; POLY: B; AXPY: X'
+    int64_t stride_a, stride_b, stride_o;
+    int32_t lda, ldb, ldo;
+    int32_t K;             // reduction length (multiple of 64)
+    int32_t tiles_m;       // tiles along M (SYRK/POLY: along the side)
+    int32_t tiles_n;       // AXPY: tiles along N
+    int32_t tiles_per_mat;
+    int32_t total_tiles;
+    float alpha;           // POLY: b (times A); AXPY: a (times X)
+    float gamma;           // POLY: c (times the product); AXPY: 1
+};
+
+hipError_t launch_momentum(const MomentumArgs& a, int32_t grad_dtype, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, int64_t count, hipStream_t s);
+hipError_t launch_normalize(const NormalizeArgs& a, hipStream_t s);
+hipError_t launch_apply(const ApplyArgs& a, hipStream_t s);
+hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s);
+
+}  // namespace muon

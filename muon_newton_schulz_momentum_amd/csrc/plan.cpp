@@ -1,0 +1,335 @@
+// Host planner: shape buckets, chunks, workspace layout and the per-matrix tables.
+//
+// This translation unit makes no HIP call; it builds with any C++17 compiler so the
+// planner can be tested on a machine without a GPU (and under sanitizers).
+//
+// The pages batch same-shape momentum matrices before the exchange and cache the
+// resharding index metadata because a MoE model has thousands of same-shape experts
+// ("Frontier Pre-training at Microsoft AI", method details section 5, resharding step 2
+// and the tuning notes after it).  On one GPU the same idea is the plan: computed once,
+// uploaded once, reused every step.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <new>
+#include <tuple>
+
+#include "plan_internal.h"
+
+namespace muon {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+muon_status set_error(muon_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+namespace {
+
+int32_t pick_tile(int64_t m) {
+    if (m >= 1024) return TILE_256;
+    if (m > 128) return TILE_128;
+    return TILE_64;
+}
+
+// Bytes one matrix adds to a chunk region: two X buffers, A and B, and the norm partials.
+uint64_t per_matrix_bytes(int64_t mp, int64_t np, int64_t ew_tiles) {
+    return 2ull * (uint64_t)mp * (uint64_t)np * 2ull      // X ping-pong (bf16)
+         + 2ull * (uint64_t)mp * (uint64_t)mp * 2ull      // A and B (bf16)
+         + (uint64_t)ew_tiles * 8ull                      // per-tile sums of squares (fp64)
+         + 8ull;                                          // 1/(||X0|| + eps) (fp64)
+}
+
+void layout_region(Chunk& c, uint64_t base) {
+    uint64_t off = base;
+    const uint64_t xb = (uint64_t)c.count * c.mp * c.np * 2ull;
+    const uint64_t ab = (uint64_t)c.count * c.mp * c.mp * 2ull;
+    c.off_xp = off; off = align_up(off + xb, WS_ALIGN);
+    c.off_xq = off; off = align_up(off + xb, WS_ALIGN);
+    c.off_a = off;  off = align_up(off + ab, WS_ALIGN);
+    c.off_b = off;  off = align_up(off + ab, WS_ALIGN);
+    c.off_part = off; off = align_up(off + (uint64_t)c.count * c.ew_tiles * 8ull, WS_ALIGN);
+    c.off_inv = off;  off = align_up(off + (uint64_t)c.count * 8ull, WS_ALIGN);
+    c.region_off = base;
+    c.region_bytes = off - base;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Interval {
+    uintptr_t lo, hi;   // [lo, hi)
+    int64_t param;
+    int role;           // 0 weight, 1 momentum, 2 grad
+};
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+const char* muon_status_string(muon_status s) {
+    switch (s) {
+        case MUON_OK: return "ok";
+        case MUON_ERR_INVALID_ARG: return "invalid argument";
+        case MUON_ERR_SHAPE: return "bad shape";
+        case MUON_ERR_ALIGNMENT: return "misaligned pointer";
+        case MUON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MUON_ERR_NOT_BOUND: return "plan not bound to a workspace";
+        case MUON_ERR_STALE_PLAN: return "stale plan";
+        case MUON_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* muon_last_error(void) { return muon::g_last_error.c_str(); }
+
+muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
+                              const muon_plan_opts* opts, muon_plan** out) {
+    clear_error();
+    if (!out) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: out is NULL");
+    *out = nullptr;
+    if (n < 0) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: n < 0");
+    if (n > 0 && !params) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: params is NULL");
+    const uint64_t cap = opts ? opts->max_workspace_bytes : 0;
+    const float* scales = opts ? opts->scale : nullptr;
+
+    // ---- validate every descriptor -----------------------------------------------------
+    std::vector<Interval> ivs;
+    for (int64_t i = 0; i < n; ++i) {
+        const muon_param_desc& d = params[i];
+        if (d.ndim != 2) continue;
+        const std::string who = "parameter " + std::to_string(i);
+        if (d.rows <= 0 || d.cols <= 0)
+            return set_error(MUON_ERR_SHAPE, who + ": rows and cols must be positive");
+        if (d.rows > (int64_t(1) << 31) || d.cols > (int64_t(1) << 31))
+            return set_error(MUON_ERR_SHAPE, who + ": dimension above 2^31");
+        if (d.grad_dtype != MUON_DTYPE_F32 && d.grad_dtype != MUON_DTYPE_BF16)
+            return set_error(MUON_ERR_INVALID_ARG, who + ": grad_dtype must be F32 or BF16");
+        if (!d.weight || !d.momentum || !d.grad)
+            return set_error(MUON_ERR_INVALID_ARG, who + ": weight, momentum and grad must be non-NULL");
+        if (!aligned16(d.weight) || !aligned16(d.momentum) || !aligned16(d.grad))
+            return set_error(MUON_ERR_ALIGNMENT, who + ": buffers must be 16-byte aligned");
+        if (scales && !std::isfinite(scales[i]))
+            return set_error(MUON_ERR_INVALID_ARG, who + ": scale must be finite");
+        const uint64_t elems = (uint64_t)d.rows * (uint64_t)d.cols;
+        const uint64_t gsz = d.grad_dtype == MUON_DTYPE_F32 ? 4 : 2;
+        ivs.push_back({(uintptr_t)d.weight, (uintptr_t)d.weight + elems * 4, i, 0});
+        ivs.push_back({(uintptr_t)d.momentum, (uintptr_t)d.momentum + elems * 4, i, 1});
+        ivs.push_back({(uintptr_t)d.grad, (uintptr_t)d.grad + elems * gsz, i, 2});
+    }
+    // Weights and momenta are written: none may overlap anything else.  Gradients are
+    // read only and may overlap each other.
+    std::sort(ivs.begin(), ivs.end(), [](const Interval& a, const Interval& b) {
+        return std::tie(a.lo, a.hi) < std::tie(b.lo, b.hi);
+    });
+    {
+        // sweep: track the written interval reaching furthest and any interval reaching furthest
+        uintptr_t reach_any = 0, reach_w = 0;
+        int64_t who_any = -1, who_w = -1;
+        for (const Interval& iv : ivs) {
+            const bool written = iv.role != 2;
+            if (reach_w > iv.lo || (written && reach_any > iv.lo)) {
+                const int64_t other = (reach_w > iv.lo) ? who_w : who_any;
+                return set_error(MUON_ERR_INVALID_ARG,
+                                 "parameters " + std::to_string(other) + " and " + std::to_string(iv.param) +
+                                     ": a weight or momentum buffer overlaps another buffer");
+            }
+            if (iv.hi > reach_any) { reach_any = iv.hi; who_any = iv.param; }
+            if (written && iv.hi > reach_w) { reach_w = iv.hi; who_w = iv.param; }
+        }
+    }
+
+    muon_plan* p = new (std::nothrow) muon_plan();
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: out of host memory");
+    p->params.resize((size_t)n);
+
+    // ---- bucket by canonical (m, n, grad dtype) ----------------------------------------
+    std::map<std::tuple<int64_t, int64_t, int32_t>, std::vector<int64_t>> buckets;
+    for (int64_t i = 0; i < n; ++i) {
+        const muon_param_desc& d = params[i];
+        ParamRec& r = p->params[(size_t)i];
+        r.ndim = d.ndim; r.grad_dtype = d.grad_dtype; r.rows = d.rows; r.cols = d.cols;
+        r.w = d.weight; r.m = d.momentum; r.g = d.grad;
+        r.included = d.ndim == 2; r.chunk = -1; r.slot = -1; r.trans = 0;
+        if (!r.included) { p->n_excluded++; continue; }
+        p->n_included++;
+        r.trans = d.rows > d.cols;
+        const int64_t m = std::min(d.rows, d.cols), nn = std::max(d.rows, d.cols);
+        buckets[{m, nn, d.grad_dtype}].push_back(i);
+    }
+    p->n_buckets = (int32_t)buckets.size();
+
+    // ---- per-bucket geometry and chunking ----------------------------------------------
+    struct BucketGeo { int64_t m, n, mp, np, ew; int32_t tile, gdt; std::vector<int64_t> members; };
+    std::vector<BucketGeo> geo;
+    for (auto& kv : buckets) {
+        BucketGeo g;
+        g.m = std::get<0>(kv.first); g.n = std::get<1>(kv.first); g.gdt = std::get<2>(kv.first);
+        g.tile = pick_tile(g.m);
+        g.mp = (int64_t)align_up((uint64_t)g.m, (uint64_t)g.tile);
+        g.np = (int64_t)align_up((uint64_t)g.n, (uint64_t)g.tile);
+        g.ew = ceil_div(g.m, EW_TILE) * ceil_div(g.n, EW_TILE);
+        if ((uint64_t)g.mp * (uint64_t)g.np >= (uint64_t(1) << 31)) {
+            delete p;
+            return set_error(MUON_ERR_SHAPE, "padded matrix " + std::to_string(g.mp) + "x" +
+                                                 std::to_string(g.np) + " exceeds 2^31 elements");
+        }
+        g.members = kv.second;
+        geo.push_back(std::move(g));
+    }
+
+    p->table_bytes = align_up((uint64_t)p->n_included * sizeof(MatEntry), WS_ALIGN);
+    uint64_t total = p->table_bytes;
+    for (const BucketGeo& g : geo)
+        total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 6 * WS_ALIGN;
+    p->shared_regions = cap != 0 && total > cap;
+
+    int32_t bucket_id = 0;
+    for (const BucketGeo& g : geo) {
+        int64_t per_chunk = (int64_t)g.members.size();
+        if (p->shared_regions) {
+            const uint64_t pm = per_matrix_bytes(g.mp, g.np, g.ew);
+            const uint64_t room = cap > p->table_bytes + 6 * WS_ALIGN ? cap - p->table_bytes - 6 * WS_ALIGN : 0;
+            const int64_t fit = (int64_t)(room / pm);
+            if (fit < 1) {
+                delete p;
+                return set_error(MUON_ERR_WORKSPACE_TOO_SMALL,
+                                 "one " + std::to_string(g.m) + "x" + std::to_string(g.n) +
+                                     " matrix needs " + std::to_string(pm + p->table_bytes + 6 * WS_ALIGN) +
+                                     " bytes of workspace; the cap is " + std::to_string(cap));
+            }
+            per_chunk = std::min(per_chunk, fit);
+        }
+        const int64_t total_m = (int64_t)g.members.size();
+        const int64_t nchunks = ceil_div(total_m, per_chunk);
+        // balanced split: chunk sizes differ by at most one
+        int64_t start = 0;
+        for (int64_t c = 0; c < nchunks; ++c) {
+            const int64_t cnt = total_m / nchunks + (c < total_m % nchunks ? 1 : 0);
+            Chunk ch{};
+            ch.bucket = bucket_id; ch.grad_dtype = g.gdt;
+            ch.m = g.m; ch.n = g.n; ch.mp = g.mp; ch.np = g.np; ch.tile = g.tile;
+            ch.count = cnt; ch.first = (int64_t)p->table.size(); ch.ew_tiles = g.ew;
+            ch.off_table = (uint64_t)ch.first * sizeof(MatEntry);
+            const int32_t cidx = (int32_t)p->chunks.size();
+            for (int64_t s = 0; s < cnt; ++s) {
+                const int64_t pi = g.members[(size_t)(start + s)];
+                ParamRec& r = p->params[(size_t)pi];
+                r.chunk = cidx; r.slot = s;
+                MatEntry e{};
+                e.w = r.w; e.m = r.m; e.g = r.g; e.rows = r.rows; e.cols = r.cols;
+                e.trans = r.trans; e.scale = scales ? scales[pi] : 1.0f;
+                p->table.push_back(e);
+            }
+            start += cnt;
+            p->chunks.push_back(ch);
+        }
+        bucket_id++;
+    }
+
+    // ---- workspace layout ---------------------------------------------------------------
+    uint64_t off = p->table_bytes, shared_max = 0;
+    for (Chunk& c : p->chunks) {
+        if (p->shared_regions) {
+            layout_region(c, p->table_bytes);
+            shared_max = std::max(shared_max, c.region_bytes);
+        } else {
+            layout_region(c, off);
+            off = c.region_off + c.region_bytes;
+        }
+    }
+    p->ws_bytes = p->shared_regions ? p->table_bytes + shared_max : off;
+    if (p->ws_bytes == 0) p->ws_bytes = WS_ALIGN;
+    *out = p;
+    return MUON_OK;
+}
+
+muon_status muon_plan_workspace_bytes(const muon_plan* plan, uint64_t* bytes) {
+    if (!plan || !bytes) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_workspace_bytes: NULL argument");
+    *bytes = plan->ws_bytes;
+    return MUON_OK;
+}
+
+muon_status muon_plan_counts(const muon_plan* plan, int32_t* n_chunks, int32_t* n_buckets,
+                             int64_t* n_included, int64_t* n_excluded) {
+    if (!plan) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_counts: plan is NULL");
+    if (n_chunks) *n_chunks = (int32_t)plan->chunks.size();
+    if (n_buckets) *n_buckets = plan->n_buckets;
+    if (n_included) *n_included = plan->n_included;
+    if (n_excluded) *n_excluded = plan->n_excluded;
+    return MUON_OK;
+}
+
+muon_status muon_plan_info(const muon_plan* plan, int32_t chunk, muon_chunk_info* out) {
+    if (!plan || !out) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_info: NULL argument");
+    if (chunk < 0 || chunk >= (int32_t)plan->chunks.size())
+        return set_error(MUON_ERR_INVALID_ARG, "muon_plan_info: chunk out of range");
+    const Chunk& c = plan->chunks[(size_t)chunk];
+    std::memset(out, 0, sizeof(*out));
+    out->m = c.m; out->n = c.n; out->m_pad = c.mp; out->n_pad = c.np; out->count = c.count;
+    out->bucket = c.bucket; out->tile = c.tile; out->grad_dtype = c.grad_dtype;
+    out->shared_region = plan->shared_regions ? 1 : 0;
+    const double m = (double)c.m, n = (double)c.n, k = (double)c.count;
+    out->flops_conventional = k * (4.0 * m * m * n + 2.0 * m * m * m);
+    out->flops_algorithmic = k * (m * (m + 1.0) * n + m * m * (m + 1.0) + 2.0 * m * m * n);
+    const double gsz = c.grad_dtype == MUON_DTYPE_F32 ? 4.0 : 2.0;
+    // momentum: read M and G, write M and X0 (bf16); apply: read W and O (bf16), write W
+    out->bytes_momentum = k * m * n * (4.0 + gsz + 4.0 + 2.0);
+    out->bytes_apply = k * m * n * (4.0 + 2.0 + 4.0);
+    out->region_offset = c.region_off;
+    out->region_bytes = c.region_bytes;
+    return MUON_OK;
+}
+
+muon_status muon_plan_param_info(const muon_plan* plan, int64_t param, muon_param_info* out) {
+    if (!plan || !out) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_param_info: NULL argument");
+    if (param < 0 || param >= (int64_t)plan->params.size())
+        return set_error(MUON_ERR_INVALID_ARG, "muon_plan_param_info: parameter index out of range");
+    std::memset(out, 0, sizeof(*out));
+    const ParamRec& r = plan->params[(size_t)param];
+    if (!r.included) return MUON_OK;
+    const Chunk& c = plan->chunks[(size_t)r.chunk];
+    out->included = 1;
+    out->chunk = r.chunk;
+    out->slot = r.slot;
+    out->transposed = r.trans;
+    out->output_offset = c.off_xp + (uint64_t)r.slot * c.mp * c.np * 2ull;
+    out->ld = c.np;
+    return MUON_OK;
+}
+
+muon_status muon_plan_validate(const muon_plan* plan, const muon_param_desc* params, int64_t n) {
+    if (!plan) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_validate: plan is NULL");
+    if (n != (int64_t)plan->params.size() || (n > 0 && !params))
+        return set_error(MUON_ERR_STALE_PLAN, "parameter count differs from the plan's");
+    for (int64_t i = 0; i < n; ++i) {
+        const muon_param_desc& d = params[i];
+        const ParamRec& r = plan->params[(size_t)i];
+        if (d.ndim != r.ndim) return set_error(MUON_ERR_STALE_PLAN, "parameter " + std::to_string(i) + ": ndim changed");
+        if (d.ndim != 2) continue;
+        if (d.rows != r.rows || d.cols != r.cols || d.grad_dtype != r.grad_dtype || d.weight != r.w ||
+            d.momentum != r.m || d.grad != r.g)
+            return set_error(MUON_ERR_STALE_PLAN, "parameter " + std::to_string(i) + ": shape, dtype or buffer changed");
+    }
+    return MUON_OK;
+}
+
+}  // extern "C"
+
+// The launch layer owns device-side state of a plan (timing events); it provides this
+// hook.  A host-only build of the planner links without it.
+extern "C" __attribute__((weak)) void muon_internal_release(muon_plan* plan);
+
+extern "C" void muon_plan_destroy(muon_plan* plan) {
+    if (!plan) return;
+    if (muon_internal_release) muon_internal_release(plan);
+    delete plan;
+}

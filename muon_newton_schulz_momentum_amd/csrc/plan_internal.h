@@ -1,0 +1,98 @@
+// Internal plan layout shared by the host planner (plan.cpp, HIP-free) and the launch
+// layer (api.hip).  Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/muon.h"
+
+namespace muon {
+
+// One matrix as the device kernels see it.  The table of these lives in the workspace
+// (uploaded once by muon_plan_bind); it is the one-GPU form of the pages' cached
+// resharding metadata.  64 bytes per row.
+struct MatEntry {
+    float* w;             // weight, rows x cols fp32
+    float* m;             // momentum, rows x cols fp32
+    const void* g;        // gradient, rows x cols (fp32 or bf16)
+    int64_t rows;
+    int64_t cols;
+    int32_t trans;        // 1: canonical X is the transpose (rows > cols)
+    float scale;          // update scale s_i
+    int64_t pad_[2];
+};
+static_assert(sizeof(MatEntry) == 64, "MatEntry layout");
+
+// Newton–Schulz tile configurations (square output tiles of edge `tile`).
+enum TileCfg : int32_t { TILE_256 = 256, TILE_128 = 128, TILE_64 = 64 };
+
+struct Chunk {
+    int32_t bucket;
+    int32_t grad_dtype;
+    int64_t m, n;            // canonical shape
+    int64_t mp, np;          // padded shape: mp multiple of tile, np multiple of 256
+    int32_t tile;
+    int64_t count;           // matrices in this chunk
+    int64_t first;           // first row of this chunk in the matrix table
+    // elementwise tiling: 64 x 64 tiles over rows x cols (same count for both orientations)
+    int64_t ew_tiles;
+    // workspace layout (byte offsets from the workspace base)
+    uint64_t region_off, region_bytes;
+    uint64_t off_xp, off_xq, off_a, off_b, off_part, off_inv;
+    uint64_t off_table;      // this chunk's first table row
+};
+
+struct ParamRec {
+    int32_t ndim;
+    int32_t grad_dtype;
+    int64_t rows, cols;
+    float* w;
+    float* m;
+    const void* g;
+    int32_t included;
+    int32_t chunk;
+    int64_t slot;
+    int32_t trans;
+};
+
+struct TimingState {
+    int32_t capacity = 0;
+    int32_t used = 0;
+    std::vector<void*> ev_begin, ev_end;       // hipEvent_t, created lazily by the launch layer
+    std::vector<int32_t> kind;
+    std::vector<double> work;
+};
+
+}  // namespace muon
+
+struct muon_plan {
+    std::vector<muon::ParamRec> params;
+    std::vector<muon::Chunk> chunks;
+    std::vector<muon::MatEntry> table;  // host copy, chunk-major
+    int32_t n_buckets = 0;
+    int64_t n_included = 0, n_excluded = 0;
+    bool shared_regions = false;
+    uint64_t table_bytes = 0;
+    uint64_t ws_bytes = 0;
+    // bind state
+    void* ws = nullptr;
+    uint64_t ws_given = 0;
+    bool bound = false;
+    muon::TimingState timing;
+};
+
+namespace muon {
+
+// Thread-local error message shared by both translation units.
+muon_status set_error(muon_status s, const std::string& msg);
+void clear_error();
+
+constexpr int EW_TILE = 64;          // elementwise tile edge
+constexpr uint64_t WS_ALIGN = 256;   // workspace sub-buffer alignment
+
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace muon

@@ -4,10 +4,10 @@ This module holds shapes, hyper-parameters and seeded random draws only — none
 Muon step's arithmetic.  Both the HIP path (through the harness) and the CPU oracle take
 their inputs from here; nothing else is shared between them.
 
-Every matrix i of workload c draws its weight, initial momentum and gradient from its
-own numpy Generator(PCG64([SEED, c, i, role])), so any single matrix can be regenerated
-on its own (the oracle recomputes sampled matrices this way, never reading GPU inputs
-back).  Per-expert gradient scales come from Generator(PCG64([SEED, c, expert, 3])).
+Every parameter i of workload c draws its weight, initial momentum and gradient from a
+torch generator of its own, seeded from (SEED, c, i, role), so any single matrix can be
+drawn again on its own.  Per-expert gradient scales come from numpy's
+Generator(PCG64([SEED, c, expert, 3])).
 
 Shapes follow the pages' architecture where they give it:
   * ladder rule: hidden = (256/3)*L and query heads = L rounded to the nearest multiple
@@ -21,6 +21,7 @@ the private MAI-Base-2 training run; no dataset or trained weight is involved.
 """
 from __future__ import annotations
 
+import hashlib
 import math
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
@@ -213,30 +214,41 @@ def _rng(cid: int, index: int, role: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64([SEED, cid, index, role]))
 
 
+def seed_of(cid: int, index: int, role: int) -> int:
+    """64-bit seed of one (workload, parameter, role) draw."""
+    h = hashlib.blake2b(f"{SEED}:{cid}:{index}:{role}".encode(), digest_size=8).digest()
+    return int.from_bytes(h, "little") & ((1 << 63) - 1)
+
+
 def group_scale(cid: int, group: int) -> float:
     """Per-expert gradient scale, log-uniform in [0.1, 10] (mimics skewed token load)."""
     u = _rng(cid, group, ROLE_SCALE).uniform(math.log(0.1), math.log(10.0))
     return float(math.exp(u))
 
 
-def generate(w: Workload, index: int, roles=("W", "M", "G")) -> dict:
-    """Seeded float32 arrays for parameter `index` of workload `w`.
+def generate(w: Workload, index: int, roles=("W", "M", "G"), device="cpu") -> dict:
+    """Seeded float32 torch tensors for parameter `index` of workload `w` on `device`.
 
-    Returns {"W": ..., "M": ..., "G": ...} (only the requested roles).  G is float32
-    here; a bf16-gradient parameter is rounded to bf16 by whoever builds its tensor.
+    Each role is N(0, std) from torch's generator on that device, seeded with
+    seed_of(cid, index, role) (on a GPU that is torch's counter-based Philox generator).
+    The draw depends on the device type, so parity tests draw on the GPU and hand the
+    oracle host copies taken before any library call.  Expert gradients are multiplied by
+    their expert's scale.  G is float32 here; a bf16-gradient parameter is rounded to
+    bf16 (nearest even) by the caller that builds its tensor.
     """
+    import torch
+
     p = w.params[index]
+    dev = torch.device(device)
     out = {}
-    if "W" in roles:
-        out["W"] = _rng(w.cid, index, ROLE_W).standard_normal(p.shape, dtype=np.float32) \
-            * np.float32(p.w_std)
-    if "M" in roles:
-        out["M"] = _rng(w.cid, index, ROLE_M).standard_normal(p.shape, dtype=np.float32) \
-            * np.float32(p.m_std)
-    if "G" in roles:
-        g = _rng(w.cid, index, ROLE_G).standard_normal(p.shape, dtype=np.float32) \
-            * np.float32(p.g_std)
-        if w.scale_groups and p.group >= 0:
-            g = g * np.float32(group_scale(w.cid, p.group))
-        out["G"] = g
+    for role, code, std in (("W", ROLE_W, p.w_std), ("M", ROLE_M, p.m_std), ("G", ROLE_G, p.g_std)):
+        if role not in roles:
+            continue
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed_of(w.cid, index, code))
+        t = torch.randn(p.shape, generator=g, device=dev, dtype=torch.float32)
+        scale = std
+        if role == "G" and w.scale_groups and p.group >= 0:
+            scale = std * group_scale(w.cid, p.group)
+        out[role] = t.mul_(float(np.float32(scale)))
     return out

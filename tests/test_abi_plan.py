@@ -1,0 +1,264 @@
+"""CPU tests of the C ABI: the library loads, exports what include/muon.h declares, and
+the host planner (no device calls) buckets, chunks and validates as documented.
+
+Device pointers here are fake, aligned addresses: the planner only records them.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from muon_newton_schulz_momentum_amd import binding as L
+from muon_newton_schulz_momentum_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def test_exports_every_declared_symbol():
+    decl = set(re.findall(r"MUON_API[^;(]*?\b(muon_\w+)\s*\(", open(HEADER).read()))
+    assert len(decl) >= 15
+    lib = C.CDLL(L.LIB_PATH)
+    for name in sorted(decl):
+        assert hasattr(lib, name), name
+    assert decl == set(L.EXPORTED)
+
+
+class FakeMem:
+    """Hands out disjoint, 256-byte aligned fake device addresses."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def take(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 255) // 256 * 256 + 256
+        return p
+
+
+def _descs(shapes, gdtype=L.MUON_DTYPE_F32, mem=None):
+    mem = mem or FakeMem()
+    arr = (L.muon_param_desc * len(shapes))()
+    for i, shp in enumerate(shapes):
+        d = arr[i]
+        d.ndim = len(shp)
+        if len(shp) == 2:
+            r, c = shp
+            d.rows, d.cols = r, c
+            d.grad_dtype = gdtype
+            d.weight = mem.take(r * c * 4)
+            d.momentum = mem.take(r * c * 4)
+            d.grad = mem.take(r * c * (4 if gdtype == L.MUON_DTYPE_F32 else 2))
+    return arr
+
+
+def _plan(arr, n=None, cap=0, scales=None):
+    opts = L.muon_plan_opts()
+    opts.max_workspace_bytes = cap
+    keep = None
+    if scales is not None:
+        keep = (C.c_float * len(scales))(*scales)
+        opts.scale = keep
+    p = C.c_void_p()
+    st = L.muon_plan_buckets(arr, len(arr) if n is None else n, C.byref(opts), C.byref(p))
+    return st, p
+
+
+def _infos(p):
+    nc = C.c_int32()
+    L.check(L.muon_plan_counts(p, C.byref(nc), None, None, None), "counts")
+    out = []
+    for c in range(nc.value):
+        info = L.muon_chunk_info()
+        L.check(L.muon_plan_info(p, c, C.byref(info)), "info")
+        out.append({f: getattr(info, f) for f, _ in L.muon_chunk_info._fields_})
+    return out
+
+
+def _pinfo(p, i):
+    info = L.muon_param_info()
+    L.check(L.muon_plan_param_info(p, i, C.byref(info)), "param_info")
+    return info
+
+
+@pytest.mark.parametrize("key", ["tiny", "ladder24", "moe_bucket", "full_width", "moe_slice"])
+def test_buckets_of_every_workload(key):
+    w = wl.get(key)
+    shapes = [p.shape for p in w.params]
+    gd = L.MUON_DTYPE_BF16 if any(p.grad_dtype == "bf16" for p in w.params) else L.MUON_DTYPE_F32
+    arr = _descs(shapes, gd)
+    st, p = _plan(arr)
+    assert st == L.MUON_OK, L.muon_last_error()
+    try:
+        nc, nb, ninc, nex = C.c_int32(), C.c_int32(), C.c_int64(), C.c_int64()
+        L.muon_plan_counts(p, C.byref(nc), C.byref(nb), C.byref(ninc), C.byref(nex))
+        want = {}
+        for s in shapes:
+            if len(s) == 2:
+                k = tuple(sorted(s))
+                want[k] = want.get(k, 0) + 1
+        assert nb.value == len(want) and nc.value == len(want)   # no cap: one chunk per bucket
+        assert ninc.value == sum(want.values())
+        assert nex.value == sum(1 for s in shapes if len(s) != 2)
+        got = {(i["m"], i["n"]): i["count"] for i in _infos(p)}
+        assert got == want
+        for i in _infos(p):
+            assert i["m_pad"] % i["tile"] == 0 and i["n_pad"] % i["tile"] == 0
+            assert i["m_pad"] >= i["m"] and i["n_pad"] >= i["n"] and i["shared_region"] == 0
+        # every 2-D parameter sits in exactly one (chunk, slot), transposed iff rows > cols
+        seen = set()
+        for idx, s in enumerate(shapes):
+            pi = _pinfo(p, idx)
+            if len(s) != 2:
+                assert pi.included == 0
+                continue
+            assert pi.included == 1 and pi.transposed == int(s[0] > s[1])
+            assert (pi.chunk, pi.slot) not in seen
+            seen.add((pi.chunk, pi.slot))
+            ci = _infos(p)[pi.chunk]
+            assert (ci["m"], ci["n"]) == tuple(sorted(s)) and 0 <= pi.slot < ci["count"]
+            assert pi.ld == ci["n_pad"] and pi.output_offset % 256 == 0
+    finally:
+        L.muon_plan_destroy(p)
+
+
+def test_flops_match_workload_accounting():
+    w = wl.get("ladder24")
+    arr = _descs([p.shape for p in w.params])
+    st, p = _plan(arr)
+    assert st == 0
+    conv = sum(i["flops_conventional"] for i in _infos(p)) * w.steps
+    alg = sum(i["flops_algorithmic"] for i in _infos(p)) * w.steps
+    L.muon_plan_destroy(p)
+    c2, a2 = w.ns_flops()
+    assert abs(conv - c2) / c2 < 1e-12 and abs(alg - a2) / a2 < 1e-12
+
+
+def test_workspace_size_formula():
+    shapes = [(64, 128)] * 3 + [(300, 70)] * 2
+    st, p = _plan(_descs(shapes))
+    assert st == 0
+    nb = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(nb))
+    table = (5 * 64 + 255) // 256 * 256
+    total = table
+    for i in _infos(p):
+        m, n, mp, np_, k = i["m"], i["n"], i["m_pad"], i["n_pad"], i["count"]
+        ew = -(-m // 64) * -(-n // 64)
+        al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+        region = 2 * al(k * mp * np_ * 2) + 2 * al(k * mp * mp * 2) + al(k * ew * 8) + al(k * 8)
+        assert i["region_bytes"] == region and i["region_offset"] == total
+        total += region
+    assert nb.value == total
+    L.muon_plan_destroy(p)
+
+
+def test_chunking_under_a_cap():
+    shapes = [(1024, 4096)] * 40 + [(4096, 1024)] * 20 + [(512, 4096)]
+    st, p = _plan(_descs(shapes))
+    full = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(full))
+    L.muon_plan_destroy(p)
+    cap = full.value // 5
+    st, p = _plan(_descs(shapes), cap=cap)
+    assert st == 0, L.muon_last_error()
+    nb = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(nb))
+    assert nb.value <= cap
+    infos = _infos(p)
+    assert len(infos) > 2 and all(i["shared_region"] == 1 for i in infos)
+    big = [i for i in infos if i["m"] == 1024]
+    assert sum(i["count"] for i in big) == 60
+    assert max(i["count"] for i in big) - min(i["count"] for i in big) <= 1
+    slots = {(_pinfo(p, k).chunk, _pinfo(p, k).slot) for k in range(len(shapes))}
+    assert len(slots) == len(shapes)
+    # chunk = -1 is refused for shared regions (checked before any device call)
+    assert L.muon_momentum_update(p, -1, 0.9, None) == L.MUON_ERR_NOT_BOUND  # not bound yet
+    L.muon_plan_destroy(p)
+    # a cap below one matrix fails cleanly
+    st, p = _plan(_descs(shapes), cap=1 << 20)
+    assert st == L.MUON_ERR_WORKSPACE_TOO_SMALL and not p.value
+
+
+def test_validation_errors():
+    mem = FakeMem()
+    arr = _descs([(8, 8)], mem=mem)
+    arr[0].rows = 0
+    assert _plan(arr)[0] == L.MUON_ERR_SHAPE
+    arr = _descs([(8, 8)], mem=mem)
+    arr[0].weight = arr[0].weight + 4
+    assert _plan(arr)[0] == L.MUON_ERR_ALIGNMENT
+    arr = _descs([(8, 8)], mem=mem)
+    arr[0].momentum = arr[0].weight
+    assert _plan(arr)[0] == L.MUON_ERR_INVALID_ARG
+    arr = _descs([(8, 8), (8, 8)], mem=mem)
+    arr[1].weight = arr[0].momentum + 64        # overlaps parameter 0's momentum
+    assert _plan(arr)[0] == L.MUON_ERR_INVALID_ARG
+    arr = _descs([(8, 8), (8, 8)], mem=mem)
+    arr[1].grad = arr[0].grad                   # shared read-only gradients are allowed
+    assert _plan(arr)[0] == L.MUON_OK
+    arr = _descs([(8, 8)], mem=mem)
+    arr[0].grad_dtype = 7
+    assert _plan(arr)[0] == L.MUON_ERR_INVALID_ARG
+    arr = _descs([(8, 8)], mem=mem)
+    arr[0].grad = None
+    assert _plan(arr)[0] == L.MUON_ERR_INVALID_ARG
+    p = C.c_void_p()
+    assert L.muon_plan_buckets(None, 3, None, C.byref(p)) == L.MUON_ERR_INVALID_ARG
+    assert L.muon_plan_buckets(None, 0, None, None) == L.MUON_ERR_INVALID_ARG
+    assert b"out" in L.muon_last_error()
+    arr = _descs([(8, 8)], mem=mem)
+    assert _plan(arr, scales=[float("nan")])[0] == L.MUON_ERR_INVALID_ARG
+    # a non-2-D parameter is excluded, not an error, and its pointers are not looked at
+    arr = _descs([(8,), (8, 8)], mem=mem)
+    st, p = _plan(arr)
+    assert st == 0
+    L.muon_plan_destroy(p)
+
+
+def test_empty_plan():
+    st, p = _plan((L.muon_param_desc * 1)(), n=0)
+    assert st == 0
+    nb = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(nb))
+    assert nb.value > 0
+    assert _infos(p) == []
+    L.muon_plan_destroy(p)
+
+
+def test_plan_is_deterministic_and_validates():
+    shapes = [(64, 128), (128, 64), (7, 300), (300, 7), (5,), (2048, 2048)]
+    mem = FakeMem()
+    arr = _descs(shapes, mem=mem)
+    st1, p1 = _plan(arr)
+    st2, p2 = _plan(arr)
+    assert st1 == st2 == 0
+    assert _infos(p1) == _infos(p2)
+    for i in range(len(shapes)):
+        a, b = _pinfo(p1, i), _pinfo(p2, i)
+        assert bytes(a) == bytes(b)
+    assert L.muon_plan_validate(p1, arr, len(shapes)) == L.MUON_OK
+    arr[2].cols = 301
+    assert L.muon_plan_validate(p1, arr, len(shapes)) == L.MUON_ERR_STALE_PLAN
+    assert L.muon_plan_validate(p1, arr, 3) == L.MUON_ERR_STALE_PLAN
+    L.muon_plan_destroy(p1)
+    L.muon_plan_destroy(p2)
+
+
+def test_step_calls_refused_before_bind_and_bind_checks():
+    st, p = _plan(_descs([(64, 128)]))
+    assert st == 0
+    assert L.muon_momentum_update(p, 0, 0.95, None) == L.MUON_ERR_NOT_BOUND
+    assert L.muon_ns_batched(p, 0, 3.4445, -4.775, 2.0315, 5, 1e-7, None) == L.MUON_ERR_NOT_BOUND
+    assert L.muon_apply(p, 0, 0.02, 0.1, None) == L.MUON_ERR_NOT_BOUND
+    assert L.muon_step(p, -1, 0.95, 3.4, -4.7, 2.0, 5, 1e-7, 0.02, 0.1, None) == L.MUON_ERR_NOT_BOUND
+    assert L.muon_plan_bind(p, None, 1 << 30, None) == L.MUON_ERR_INVALID_ARG
+    assert L.muon_plan_bind(p, 1 << 40 | 16, 1 << 30, None) == L.MUON_ERR_ALIGNMENT
+    assert L.muon_plan_bind(p, 1 << 40, 16, None) == L.MUON_ERR_WORKSPACE_TOO_SMALL
+    assert L.muon_plan_info(p, 5, C.byref(L.muon_chunk_info())) == L.MUON_ERR_INVALID_ARG
+    assert L.muon_plan_param_info(p, -1, C.byref(L.muon_param_info())) == L.MUON_ERR_INVALID_ARG
+    assert L.muon_kernel_name(L.MUON_KERNEL_GEMM_AXPY) == b"gemm_axpy"
+    assert L.muon_status_string(L.MUON_ERR_STALE_PLAN) == b"stale plan"
+    L.muon_plan_destroy(p)
+    L.muon_plan_destroy(None)

@@ -1,0 +1,301 @@
+"""GPU parity: libmuon's HIP path (through the C ABI) against the float64 CPU oracle.
+
+Bars (per matrix):
+  * momentum: bitwise equal float32 M;
+  * Newton–Schulz output O: ||O_gpu - O_ref||_F / ||O_ref||_F <= 1e-2 against the oracle in
+    bf16-emulating mode (the GPU accumulates bf16 products in float32, the oracle in float64);
+  * apply: bitwise equal float32 W when the oracle applies the GPU's own O (so NS
+    differences do not leak into the apply check).
+Inputs are drawn on the GPU from the seeded workload generator; the oracle receives host
+copies taken before any library call.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from oracle import muon_oracle as orc  # noqa: E402
+
+NS_TOL = 1e-2
+A, B, C, K, EPS = 3.4445, -4.7750, 2.0315, 5, 1e-7
+
+
+@pytest.fixture(scope="module")
+def mm():
+    from muon_newton_schulz_momentum_amd import harness, workloads
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return harness, workloads
+
+
+def _host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 \
+        else t.detach().cpu().numpy()
+
+
+def _rel(a, b):
+    nb = np.linalg.norm(b)
+    return np.linalg.norm(a - b) / (nb if nb > 0 else 1.0)
+
+
+def _make(shapes, seed, gdtype=torch.float32, w_std=0.02, g_std=1e-3, m_std=1e-3):
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    out = []
+    for s in shapes:
+        W = torch.randn(s, generator=gen, device="cuda") * w_std
+        M = torch.randn(s, generator=gen, device="cuda") * m_std
+        G = (torch.randn(s, generator=gen, device="cuda") * g_std).to(gdtype)
+        out.append(ParamTensors(W, M, G))
+    return out
+
+
+def _snapshot(params):
+    return [(_host(p.weight), _host(p.momentum), _host(p.grad)) for p in params]
+
+
+def _check_step(plan, params, snap, beta, lr, wd, scales=None, ns_tol=NS_TOL, indices=None,
+                steps=K):
+    """Compare one completed GPU step with the oracle for the given parameter indices."""
+    worst = 0.0
+    for i in (range(len(params)) if indices is None else indices):
+        W0, M0, G0 = snap[i]
+        if W0.ndim != 2:
+            np.testing.assert_array_equal(_host(params[i].weight), W0)
+            continue
+        M_ref, X0 = orc.momentum_update(M0, G0, beta)
+        M_gpu = _host(params[i].momentum)
+        assert np.array_equal(M_gpu.view(np.uint32), M_ref.view(np.uint32)), f"momentum of param {i}"
+        O_ref = orc.newton_schulz(X0, A, B, C, steps, EPS, emulate_bf16=True)
+        O_gpu = _host(plan.output_oriented(i))
+        r = _rel(O_gpu, O_ref)
+        worst = max(worst, r)
+        assert r <= ns_tol, f"param {i} shape {W0.shape}: NS relative error {r:.3e}"
+        s = 1.0 if scales is None else scales[i]
+        W_ref = orc.apply_update(W0, O_gpu, lr, wd, s)
+        W_gpu = _host(params[i].weight)
+        bad = np.flatnonzero(W_gpu.view(np.uint32) != W_ref.view(np.uint32))
+        assert bad.size == 0, f"apply of param {i}: {bad.size} elements differ, e.g. {W_gpu.flat[bad[0]]} vs {W_ref.flat[bad[0]]}"
+    return worst
+
+
+def _run(plan, beta, lr, wd, steps=K, split=True):
+    if split:
+        plan.momentum_update(beta)
+        plan.ns_batched(A, B, C, steps, EPS)
+        plan.apply(lr, wd)
+    else:
+        plan.step(beta, lr, wd, A, B, C, steps, EPS)
+    torch.cuda.synchronize()
+
+
+def test_tiny_workload_full_step(mm):
+    harness, wl = mm
+    w = wl.get("tiny")
+    params = harness.make_params(w)
+    snap = _snapshot(params)
+    plan = harness.Plan(params)
+    _run(plan, w.beta, w.lr, w.wd)
+    worst = _check_step(plan, params, snap, w.beta, w.lr, w.wd)
+    print(f"tiny: worst NS rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("shapes", [
+    [(300, 700), (700, 300), (5, 9)],                 # 128-tiles, ragged, both orientations
+    [(1100, 2300)],                                   # 256-tiles with a ragged tail
+    [(1, 4096), (4096, 1), (2, 3000), (32, 4096)],    # degenerate small buckets
+    [(65, 130), (130, 65), (64, 64), (127, 129)],     # 64-tiles around the edges
+    [(257, 257), (1024, 1030)],
+])
+def test_ragged_shapes(mm, shapes):
+    harness, _ = mm
+    params = _make(shapes, seed=len(shapes) * 7 + shapes[0][0])
+    snap = _snapshot(params)
+    plan = harness.Plan(params)
+    _run(plan, 0.95, 0.02, 0.1)
+    _check_step(plan, params, snap, 0.95, 0.02, 0.1)
+
+
+def test_bf16_gradients_and_update_scales(mm):
+    harness, _ = mm
+    shapes = [(256, 1024), (1024, 256), (512, 512)]
+    params = _make(shapes, seed=11, gdtype=torch.bfloat16)
+    scales = [0.5, 2.0, 1.25]
+    snap = _snapshot(params)
+    plan = harness.Plan(params, scales=scales)
+    lr, wd = 9.3e-4, 0.1832
+    _run(plan, 0.95, lr, wd, split=False)
+    _check_step(plan, params, snap, 0.95, lr, wd, scales=scales)
+
+
+def test_one_dimensional_params_untouched(mm):
+    harness, _ = mm
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+    params = _make([(64, 128)], seed=3)
+    v = torch.randn(4096, device="cuda")
+    params.append(ParamTensors(v.clone(), v.clone(), v.clone()))
+    snap = _snapshot(params)
+    plan = harness.Plan(params)
+    assert plan.n_excluded == 1
+    _run(plan, 0.9, 0.02, 0.1)
+    _check_step(plan, params, snap, 0.9, 0.02, 0.1)
+    np.testing.assert_array_equal(_host(params[1].momentum), snap[1][1])
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3])
+def test_step_count_parity(mm, steps):
+    harness, _ = mm
+    params = _make([(200, 600), (600, 200)], seed=40 + steps)
+    snap = _snapshot(params)
+    plan = harness.Plan(params)
+    _run(plan, 0.95, 0.02, 0.1, steps=steps)
+    _check_step(plan, params, snap, 0.95, 0.02, 0.1, steps=steps)
+
+
+def test_several_optimizer_steps(mm):
+    harness, _ = mm
+    params = _make([(128, 384), (384, 128)], seed=5)
+    plan = harness.Plan(params)
+    for it in range(3):
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(100 + it)
+        for p in params:
+            p.grad.copy_(torch.randn(p.grad.shape, generator=gen, device="cuda") * 1e-3)
+        snap = _snapshot(params)
+        _run(plan, 0.95, 0.02, 0.1)
+        _check_step(plan, params, snap, 0.95, 0.02, 0.1)
+
+
+def test_beta_zero_feeds_gradient_to_ns(mm):
+    harness, _ = mm
+    params = _make([(96, 160)], seed=8)
+    snap = _snapshot(params)
+    plan = harness.Plan(params)
+    _run(plan, 0.0, 0.02, 0.1)
+    np.testing.assert_array_equal(_host(params[0].momentum), snap[0][2])
+    _check_step(plan, params, snap, 0.0, 0.02, 0.1)
+
+
+def test_zero_matrix_gives_zero_update(mm):
+    harness, _ = mm
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+    W = torch.randn(64, 256, device="cuda")
+    p = ParamTensors(W.clone(), torch.zeros(64, 256, device="cuda"), torch.zeros(64, 256, device="cuda"))
+    plan = harness.Plan([p])
+    _run(plan, 0.95, 0.5, 0.1)
+    assert torch.count_nonzero(plan.output(0).float()) == 0
+    ref = orc.apply_update(_host(W), np.zeros((64, 256)), 0.5, 0.1)
+    np.testing.assert_array_equal(_host(p.weight), ref)
+
+
+def test_nan_stays_in_its_matrix(mm):
+    harness, _ = mm
+    params = _make([(128, 256), (128, 256), (128, 256)], seed=9)
+    params[1].grad[3, 7] = float("nan")
+    snap = _snapshot(params)
+    plan = harness.Plan(params)
+    _run(plan, 0.95, 0.02, 0.1)
+    assert torch.isnan(params[1].weight).any()
+    for i in (0, 2):
+        assert torch.isfinite(params[i].weight).all()
+    _check_step(plan, params, snap, 0.95, 0.02, 0.1, indices=[0, 2])
+
+
+def test_determinism_and_batch_invariance(mm):
+    harness, _ = mm
+    shapes = [(512, 2048)] * 4 + [(2048, 512)] * 2
+    base = _make(shapes, seed=12)
+    snap = _snapshot(base)
+
+    def fresh(idx):
+        from muon_newton_schulz_momentum_amd.harness import ParamTensors
+        return [ParamTensors(torch.from_numpy(snap[i][0]).cuda(), torch.from_numpy(snap[i][1]).cuda(),
+                             torch.from_numpy(snap[i][2]).cuda()) for i in idx]
+
+    outs = []
+    for _ in range(2):
+        ps = fresh(range(len(shapes)))
+        plan = harness.Plan(ps)
+        _run(plan, 0.95, 0.02, 0.1)
+        outs.append([plan.output(i).clone() for i in range(len(shapes))] + [p.weight.clone() for p in ps])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b), "two identical runs differ"
+    # matrix 2 alone, and matrix 4 alone (transposed), give the same bits as in the bucket
+    for i in (2, 4):
+        ps = fresh([i])
+        plan = harness.Plan(ps)
+        _run(plan, 0.95, 0.02, 0.1)
+        assert torch.equal(plan.output(0), outs[0][i])
+        assert torch.equal(ps[0].weight, outs[0][len(shapes) + i])
+
+
+def test_transpose_equivariance_is_bitwise(mm):
+    harness, _ = mm
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+    p0 = _make([(192, 448)], seed=13)[0]
+    p1 = ParamTensors(p0.weight.t().contiguous(), p0.momentum.t().contiguous(), p0.grad.t().contiguous())
+    plan = harness.Plan([p0, p1])
+    _run(plan, 0.95, 0.02, 0.1)
+    assert torch.equal(plan.output(0), plan.output(1))
+    assert torch.equal(p0.weight, p1.weight.t())
+
+
+def test_chunked_workspace_equals_unchunked(mm):
+    harness, _ = mm
+    shapes = [(256, 1024)] * 6 + [(1024, 256)] * 3 + [(64, 128)] * 2
+    base = _make(shapes, seed=14)
+    snap = _snapshot(base)
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+
+    def fresh():
+        return [ParamTensors(torch.from_numpy(s[0]).cuda(), torch.from_numpy(s[1]).cuda(),
+                             torch.from_numpy(s[2]).cuda()) for s in snap]
+    ps_full = fresh()
+    full = harness.Plan(ps_full)
+    _run(full, 0.95, 0.02, 0.1)
+    ps_cap = fresh()
+    capped = harness.Plan(ps_cap, max_workspace_bytes=full.workspace_bytes // 3)
+    assert capped.n_chunks > full.n_chunks
+    for ch in range(capped.n_chunks):
+        capped.momentum_update(0.95, chunk=ch)
+        capped.ns_batched(A, B, C, K, EPS, chunk=ch)
+        capped.apply(0.02, 0.1, chunk=ch)
+    torch.cuda.synchronize()
+    for a, b in zip(ps_full, ps_cap):
+        assert torch.equal(a.weight, b.weight) and torch.equal(a.momentum, b.momentum)
+    # muon_step with chunk -1 walks the shared chunks in order
+    ps_step = fresh()
+    stepped = harness.Plan(ps_step, max_workspace_bytes=full.workspace_bytes // 3)
+    stepped.step(0.95, 0.02, 0.1)
+    torch.cuda.synchronize()
+    for a, b in zip(ps_full, ps_step):
+        assert torch.equal(a.weight, b.weight)
+
+
+def test_ladder24_sampled_matrices(mm):
+    """The benchmark's workload at full size: every matrix stepped, a sample checked."""
+    harness, wl = mm
+    w = wl.get("ladder24")
+    params = harness.make_params(w)
+    sample = [0, 4, 6, 83, 160, 166]        # both buckets, both orientations
+    snap = {i: (_host(params[i].weight), _host(params[i].momentum), _host(params[i].grad)) for i in sample}
+    plan = harness.Plan(params)
+    _run(plan, w.beta, w.lr, w.wd)
+    worst = _check_step(plan, params, snap, w.beta, w.lr, w.wd, indices=sample)
+    print(f"ladder24 sampled: worst NS rel err {worst:.2e}")
+
+
+def test_kernel_timing_records_launches(mm):
+    harness, _ = mm
+    from muon_newton_schulz_momentum_amd import binding as L
+    params = _make([(256, 512)] * 2, seed=15)
+    plan = harness.Plan(params)
+    plan.timing_enable(64)
+    _run(plan, 0.95, 0.02, 0.1)
+    ms, n, work = plan.timing_read(L.MUON_KERNEL_GEMM_AXPY)
+    assert n == K and ms > 0 and work == pytest.approx(K * 2 * 2.0 * 256 * 256 * 512)
+    ms, n, work = plan.timing_read(L.MUON_KERNEL_MOMENTUM)
+    assert n == 1 and work == 2 * 256 * 512 * 14
