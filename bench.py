@@ -1,0 +1,259 @@
+"""Benchmark of one Muon optimizer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload ladder24] [--gpus 1]
+
+A step is the whole hot path over every 2-D matrix of the workload: momentum update +
+bf16 cast, Frobenius normalisation, k quintic Newton–Schulz iterations (SYRK, SYRK+poly,
+GEMM+axpy per iteration), and the float32 apply with decoupled weight decay — all in
+libmuon's HIP kernels, with inputs resident in HBM.  W untimed steps run first; then K
+steps are timed between device synchronisations.  Prints one JSON line.
+
+  value        effective NS TFLOP/s over the whole step: conventional Newton–Schulz FLOPs
+               (4 m^2 n + 2 m^3 per iteration and matrix) / step time
+  roofline     the kernel that takes the most time, from HIP events recorded around each
+               of its launches on its own stream during the timed steps: algorithmic
+               FLOPs (or bytes) per launch / mean launch time, against MI355X's published
+               peak (bf16 dense MFMA 2.5 PFLOP/s; HBM 8 TB/s)
+  cpu_baseline the float64 CPU oracle (test infrastructure, untuned) on a bounded sample
+               of the same workload, extrapolated per bucket; also a parity check of the
+               sampled matrices' first step
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "ladder24"
+METRIC = "batched Newton–Schulz TFLOP/s (% bf16 MFMA peak) + Muon step ms per shape mix"
+KERNEL_SOURCES = ["ns_gemm.hip", "elementwise.hip", "api.hip", "kernels.h", "device_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "muon_newton_schulz_momentum_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    if data.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = data.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path's sharding across GPUs is described, not built)"}))
+        return 2
+    if args.steps < 1 or args.warmup < 1:
+        print(json.dumps({"error": "--steps and --warmup must be >= 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    from muon_newton_schulz_momentum_amd import binding as L
+    from muon_newton_schulz_momentum_amd import harness, workloads as wl
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 2
+    torch.cuda.set_device(0)
+    w = wl.get(args.workload)
+    t0 = time.time()
+    params = harness.make_params(w, device="cuda")
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+
+    # bounded oracle sample: first, middle and last matrix of every canonical bucket
+    buckets = {}
+    for i, p in enumerate(w.params):
+        if p.is_matrix:
+            buckets.setdefault(tuple(sorted(p.shape)), []).append(i)
+    sample = {}
+    for key, idx in buckets.items():
+        pick = sorted({idx[0], idx[len(idx) // 2], idx[-1]})
+        sample[key] = pick
+    snap = {}
+    if not args.no_cpu_baseline:
+        for idx in sample.values():
+            for i in idx:
+                snap[i] = tuple(t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else
+                                t.detach().cpu().numpy() for t in (params[i].weight, params[i].momentum, params[i].grad))
+
+    plan = harness.Plan(params)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        plan.step(w.beta, w.lr, w.wd, w.a, w.b, w.c, w.steps, w.eps)
+
+    # first warm-up step: its outputs are the sampled parity check
+    step()
+    torch.cuda.synchronize()
+    first = {}
+    for i in snap:
+        first[i] = (plan.output_oriented(i).float().cpu().numpy().astype(np.float64),
+                    params[i].momentum.cpu().numpy(), params[i].weight.cpu().numpy())
+    for _ in range(args.warmup - 1):
+        step()
+    torch.cuda.synchronize()
+
+    launches_per_step = sum(3 + 3 * w.steps + 1 for _ in range(plan.n_chunks)) + 2
+    plan.timing_enable(launches_per_step * args.steps + 16)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    kernels = {}
+    for k in range(L.MUON_KERNEL_COUNT):
+        ms, n, work = plan.timing_read(k)
+        if n == 0:
+            continue
+        name = L.muon_kernel_name(k).decode()
+        mfma = k in (L.MUON_KERNEL_SYRK, L.MUON_KERNEL_SYRK_POLY, L.MUON_KERNEL_GEMM_AXPY)
+        rate = work / (ms * 1e-3) / (1e12 if mfma else 1e9)
+        peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS
+        kernels[name] = {
+            "ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+            "mean_launch_ms": ms / n, "work_per_launch": work / n,
+            "achieved": rate, "unit": "TFLOP/s" if mfma else "GB/s", "frac": rate / peak,
+            "bound": "mfma" if mfma else "hbm",
+        }
+    plan.timing_enable(0)
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    roofline = {
+        "kernel": dom, "bound": dk["bound"], "achieved": round(dk["achieved"], 2),
+        "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
+        "frac": round(dk["frac"], 4), "traffic": load_traffic(dom, w.key),
+        "work_per_launch": dk["work_per_launch"], "mean_launch_ms": dk["mean_launch_ms"],
+    }
+
+    conv, alg = w.ns_flops()
+    ns_ms = sum(kernels[k]["ms_per_step"] for k in ("syrk", "syrk_poly", "gemm_axpy", "normalize", "norm_finalize")
+                if k in kernels)
+    value = conv / (ms_per_step * 1e-3) / 1e12
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---- CPU oracle: timing on the sample, and parity of the sampled first step -------
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        from oracle import muon_oracle as orc
+        per_bucket = {}
+        worst, bitwise_ok = 0.0, True
+        for key, idx in sample.items():
+            times = []
+            for i in idx:
+                W0, M0, G0 = snap[i]
+                t1 = time.perf_counter()
+                ref = orc.muon_step_ref(W0, M0, G0, beta=w.beta, a=w.a, b=w.b, c=w.c, steps=w.steps,
+                                        eps=w.eps, lr=w.lr, wd=w.wd)
+                times.append(time.perf_counter() - t1)
+                O_gpu, M_gpu, W_gpu = first[i]
+                worst = max(worst, float(np.linalg.norm(O_gpu - ref["O"]) / np.linalg.norm(ref["O"])))
+                bitwise_ok &= bool(np.array_equal(M_gpu, ref["M"]))
+                bitwise_ok &= bool(np.array_equal(W_gpu, orc.apply_update(W0, O_gpu, w.lr, w.wd)))
+            per_bucket[key] = float(np.median(times))
+        oracle_step_s = sum(per_bucket[k] * len(buckets[k]) for k in buckets)
+        n_sample = sum(len(v) for v in sample.values())
+        cpu = {
+            "value": round(conv / oracle_step_s / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{n_sample} matrices (first, middle, last of each of {len(buckets)} buckets), "
+                      f"one full float64 step each; step time extrapolated as sum over buckets of "
+                      f"count x median per-matrix time = {oracle_step_s:.1f} s",
+            "ms_per_step": oracle_step_s * 1e3,
+        }
+        parity = {"sampled_matrices": n_sample, "ns_worst_rel_frobenius": worst, "ns_tolerance": 1e-2,
+                  "momentum_and_apply_bitwise": bitwise_ok, "ok": bool(worst <= 1e-2 and bitwise_ok)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, sigma) draws on the GPU; no dataset, no trained weights)",
+        "config": {
+            "workload": w.key, "description": w.description,
+            "matrices": len(w.matrices), "buckets": plan.n_buckets, "chunks": plan.n_chunks,
+            "ns_iterations": w.steps, "coefficients": [w.a, w.b, w.c], "beta": w.beta,
+            "lr": w.lr, "wd": w.wd, "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "ns": {
+            "ms_per_step": round(ns_ms, 4),
+            "effective_tflops_conventional": round(conv / (ns_ms * 1e-3) / 1e12, 2),
+            "algorithmic_tflops": round(alg / (ns_ms * 1e-3) / 1e12, 2),
+            "algorithmic_frac_of_peak": round(alg / (ns_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "conventional_flops_per_step": conv, "algorithmic_flops_per_step": alg,
+        },
+        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "parity": parity,
+        "input_generation_s": round(gen_s, 2),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out))
+    plan.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
