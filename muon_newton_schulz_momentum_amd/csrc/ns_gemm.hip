@@ -13,25 +13,30 @@
 //   * NS_AXPY  X' = a X + B X: a full GEMM with the axpy fused into its epilogue.
 //
 // Main loop (all three modes): one TILE x TILE output tile per workgroup, K in steps of
-// 64, two LDS stages.  Operand tiles go from global memory straight into LDS with
-// global_load_lds_dwordx4 (no VGPR staging): each lane's 16 bytes land at the
-// instruction's LDS base + 16 * lane, and the lane picks which global 16 bytes to fetch,
-// so the LDS image can be XOR-swizzled for conflict-free reads.  The next K step's loads
-// are in flight while the current step's v_mfma_f32_32x32x16_bf16 run.
+// BK through a ring of STAGES LDS buffers.  Operand tiles go from global memory straight
+// into LDS with global_load_lds_dwordx4 (no VGPR staging): each lane's 16 bytes land at
+// the instruction's LDS base + 16 * lane, and the lane picks which global 16 bytes to
+// fetch, so the LDS image can be XOR-swizzled for conflict-free reads.  Loads run
+// STAGES - 1 K steps ahead of the v_mfma_f32_32x32x16_bf16 that consume them (256 x 256
+// tiles: 2 stages of BK = 64, 128 KB; measured faster on gfx950 than 4 stages of BK = 32,
+// whose extra barriers cost more than the deeper prefetch saves).
 //   * Row-panel operands (K contiguous: X in SYRK, A in POLY, B in AXPY) are stored as
-//     rows of 64 bf16 (128 B) whose eight 16-byte chunks are permuted by chunk ^ (row % 8);
-//     an MFMA operand is one ds_read_b128 per lane.
+//     rows of BK bf16 whose 16-byte chunks are permuted per row so that the 16 lanes the
+//     LDS serves together (64 banks, one ds_read_b128 each) never share a bank.  An MFMA
+//     operand is one ds_read_b128 per lane.
 //   * The K x N operand of NS_AXPY (X, N contiguous) is stored as rows of TILE bf16 in its
 //     own orientation, with 64-byte granules permuted per row, and read with
 //     ds_read_b64_tr_b16, which transposes 4 x 4 blocks of 16-bit values across each group
 //     of 16 lanes into exactly the K-packed layout the MFMA wants.
+//   * Each MFMA is followed by at most one LDS read or load instruction (the issue order
+//     is pinned with scheduling barriers), so those issue while the matrix pipe is busy.
 //
 // Matrices are padded to multiples of TILE with zero rows and columns, so no kernel
 // needs a bounds check: zero padding stays zero through all three products.
 //
 // Workgroups are remapped so that the tiles of one matrix run on the same XCD (the
 // hardware hands consecutive workgroup ids to the 8 XCDs in turn), keeping a matrix's
-// panels in that XCD's L2.
+// panels in that XCD's L2, and tiles are ordered in groups that share operand panels.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -43,10 +48,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void global_void;
-
-constexpr int BK = 64;          // K step (bf16 elements)
 constexpr int NUM_XCD = 8;
 
 __device__ __forceinline__ int xcd_remap(int b, int g) {
@@ -55,63 +56,114 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
     return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-// Upper-triangle tile t of a T x T tile grid, row-major: row i holds tiles (i, i..T-1).
+// Tile order.  The 32 tiles an XCD runs at once should share as few operand panels as
+// possible (each panel K-slice is then fetched into that XCD's L2 once and reused).
+constexpr int GROUP = 8;
+
+// Full tm x tn grid (NS_AXPY): bands of GROUP tile rows, each band walked column by
+// column, so concurrent tiles form a GROUP-tall block (GROUP + 32/GROUP panels).
+__device__ __forceinline__ void grid_decode(int t, int tm, int tn, int& ti, int& tj) {
+    const int band = t / (GROUP * tn);
+    const int r0 = band * GROUP;
+    const int gm = min(GROUP, tm - r0);
+    const int w = t - band * GROUP * tn;
+    tj = w / gm;
+    ti = r0 + (w - tj * gm);
+}
+
+// Upper triangle of a T x T tile grid (NS_SYRK, NS_POLY): GROUP x GROUP super-blocks
+// (I <= J) in row-major order; inside a block, its tiles with i <= j row by row.
 __device__ __forceinline__ void tri_decode(int t, int T, int& ti, int& tj) {
-    int i = 0;
-    while (t >= T - i) { t -= T - i; ++i; }
-    ti = i;
-    tj = i + t;
+    const int NB = (T + GROUP - 1) / GROUP;
+    for (int I = 0; I < NB; ++I) {
+        const int rows = min(GROUP, T - I * GROUP);
+        for (int J = I; J < NB; ++J) {
+            const int cols = min(GROUP, T - J * GROUP);
+            const int cnt = (I == J) ? rows * (rows + 1) / 2 : rows * cols;
+            if (t < cnt) {
+                if (I == J) {
+                    int i = 0;
+                    while (t >= rows - i) { t -= rows - i; ++i; }
+                    ti = I * GROUP + i;
+                    tj = I * GROUP + i + t;
+                } else {
+                    ti = I * GROUP + t / cols;
+                    tj = J * GROUP + t % cols;
+                }
+                return;
+            }
+            t -= cnt;
+        }
+    }
+    ti = tj = 0;   // not reached for t < T(T+1)/2
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
-// vmcnt(0) and lgkmcnt(0): this wave's direct-to-LDS loads have landed and its LDS reads
-// have returned, so after the barrier other waves may overwrite the stage it read.
-__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0x0070); }
-
-// 16 bytes from global memory into LDS at base + 16 * lane (base wave-uniform).
-__device__ __forceinline__ void load_to_lds(const uint16_t* src, uint16_t* lds_base) {
-    __builtin_amdgcn_global_load_lds((global_void*)src, (lds_void*)lds_base, 16, 0, 0);
+// s_waitcnt with vmcnt(N) (gfx9 encoding: low 4 bits, high 2 bits at 15:14), expcnt
+// left open and lgkmcnt(0) or left open.
+template <int N, bool LGKM0>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    constexpr int imm = (N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (LGKM0 ? 0 : (15 << 8));
+    __builtin_amdgcn_s_waitcnt(imm);
 }
 
-// ds_read_b64_tr_b16 issued as inline assembly.  Through the compiler intrinsic, every
-// such read would first wait for all outstanding direct-to-LDS loads (the compiler cannot
-// tell that they target the other stage), which would expose the global-load latency
-// once per K step.  Issued this way the compiler does not track the read; its result is
-// released by lds_wait_tied() below, whose register operands carry the dependency to
-// the MFMAs that consume it.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
-    const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)p;
-    uint2 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
+// 16 bytes from global memory into LDS at base + 16 * lane (base wave-uniform), issued
+// as inline assembly so that the compiler does not track it: through the compiler
+// intrinsic, every later LDS read would first wait for all outstanding direct-to-LDS
+// loads (the compiler cannot tell that they target other stages), exposing the
+// global-load latency at every read.  Completion is therefore waited for explicitly
+// (wait_vm) before the barrier that publishes a stage.  The LDS base goes through M0;
+// nothing else in these kernels uses M0.
+__device__ __forceinline__ void load_to_lds(const uint16_t* src, const uint16_t* lds_base) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
+    // one wait state between writing M0 and the LDS-DMA instruction that reads it
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "memory");
 }
 
-// Row of the 64-byte granule swizzle for the K x N operand: the 8 rows one transposing
-// read touches (k0..k0+3 and k0+8..k0+11) get 8 different granules.
+// ds_read_b64_tr_b16: 4 x 4 blocks of 16-bit values transposed across each group of 16
+// lanes (lane 4a+b receives element b of the 8-byte rows addressed by lanes a, a+4,
+// a+8, a+12).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t* p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(const __attribute__((address_space(3))) uint16_t*)p);
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// Granule swizzle of the K x N operand: the 8 rows one transposing read touches
+// (k0..k0+3 and k0+8..k0+11) get 8 different 64-byte granules.
 __device__ __forceinline__ int kn_swz(int k) { return (k & 3) | ((k >> 1) & 4); }
 
 // Granule swizzle of the epilogue input tile: a transposing read there touches 8
 // consecutive rows, which get 8 different granules.
 __device__ __forceinline__ int ep_swz(int r) { return r & 7; }
 
-template <int MODE, int TILE, int WM, int WN>
+template <int MODE, int TILE, int WM, int WN, int BK, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = TILE / WM, WTN = TILE / WN;   // wave tile
     constexpr int FM = WTM / 32, FN = WTN / 32;       // 32 x 32 MFMA blocks per wave
     constexpr int PANEL = TILE * BK;                  // elements of one operand tile
-    constexpr int RP_INSTR = TILE / 8;                // 1 KB load instructions per row-panel tile
+    // row panels: rows of BK bf16
+    constexpr int CPR = BK / 8;                       // 16-byte chunks per row
+    constexpr int RPI = 512 / BK;                     // rows per 1 KB load instruction
+    constexpr int RP_INSTR = TILE / RPI;
     constexpr int RP_PER_WAVE = RP_INSTR / NW;
-    constexpr int KN_ROWS_PER_INSTR = 512 / TILE;     // K x N tile rows per 1 KB instruction
+    constexpr int ROWS_PER_BANKLINE = 256 / (2 * BK); // rows sharing one 64-bank line
+    // K x N panel: rows of TILE bf16
+    constexpr int KN_ROWS_PER_INSTR = 512 / TILE;
     constexpr int KN_INSTR = BK / KN_ROWS_PER_INSTR;
     constexpr int KN_PER_WAVE = KN_INSTR / NW;
-    constexpr int KN_CHUNKS = TILE / 8;               // 16-byte chunks per K x N row
+    constexpr int KN_CHUNKS = TILE / 8;
     constexpr int KN_NG = TILE / 32;                  // 64-byte granules per K x N row
+    constexpr int KSUB = BK / 16;                     // MFMA K sub-steps per K step
     static_assert(FM >= 1 && FN >= 1, "tile configuration");
     static_assert(RP_PER_WAVE >= 1 && RP_INSTR % NW == 0, "row-panel load split");
     static_assert(MODE != NS_AXPY || (KN_PER_WAVE >= 1 && KN_INSTR % NW == 0), "K x N load split");
+    static_assert(STAGES >= 2 && KSUB >= 1, "pipeline");
+    static_assert(TILE * TILE <= STAGES * 2 * PANEL, "epilogue tile fits in the stages");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][PANEL];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][2][PANEL];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -122,8 +174,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     const int t = b - mat * p.tiles_per_mat;
     int ti, tj;
     if (MODE == NS_AXPY) {
-        ti = t / p.tiles_n;
-        tj = t - ti * p.tiles_n;
+        grid_decode(t, p.tiles_m, p.tiles_n, ti, tj);
     } else {
         tri_decode(t, p.tiles_m, ti, tj);
     }
@@ -134,20 +185,20 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
                              ? p.opb + (int64_t)mat * p.stride_b + (int64_t)tj * TILE
                              : p.opb + (int64_t)mat * p.stride_b + (int64_t)tj * TILE * p.ldb;
 
+    // Chunk permutation of a row-panel row: 16 consecutive rows at one logical chunk
+    // land in 16 different 16-byte bank groups.
+    auto rp_swz = [](int row) { return (row / ROWS_PER_BANKLINE) % CPR; };
+
     // ---- per-lane source offsets of the direct-to-LDS loads (fixed across K steps) ----
-    // Row panel: instruction q covers rows 8q..8q+7; lane -> row 8q + lane/8, physical
-    // chunk lane%8 holding logical chunk (lane%8) ^ (lane/8).
     int64_t ra_off[RP_PER_WAVE], rb_off[RP_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < RP_PER_WAVE; ++i) {
         const int q = wave + NW * i;
-        const int row = 8 * q + (lane >> 3);
-        const int chunk = (lane & 7) ^ (lane >> 3);
+        const int row = RPI * q + lane / CPR;
+        const int chunk = (lane % CPR) ^ rp_swz(row);
         ra_off[i] = (int64_t)row * p.lda + chunk * 8;
         rb_off[i] = (int64_t)row * p.ldb + chunk * 8;
     }
-    // K x N panel (NS_AXPY): instruction q covers rows q*KN_ROWS_PER_INSTR..; lane ->
-    // row within the instruction lane / KN_CHUNKS, physical chunk lane % KN_CHUNKS.
     int64_t kn_off[MODE == NS_AXPY ? KN_PER_WAVE : 1];
     if (MODE == NS_AXPY) {
 #pragma unroll
@@ -160,21 +211,19 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
         }
     }
 
-    auto issue_loads = [&](int kt, int s) {
+    // One direct-to-LDS load instruction (index d of this wave's NDMA per K step) of K
+    // step kt into stage st.
+    constexpr int NDMA = RP_PER_WAVE + ((MODE == NS_AXPY) ? KN_PER_WAVE : RP_PER_WAVE);
+    auto dma = [&](int d, int kt, int st) {
         const int k0 = kt * BK;
-        uint16_t* As = smem[s][0];
-        uint16_t* Bs = smem[s][1];
-#pragma unroll
-        for (int i = 0; i < RP_PER_WAVE; ++i)
-            load_to_lds(Ag + ra_off[i] + k0, As + (wave + NW * i) * 512);
-        if (MODE == NS_AXPY) {
-#pragma unroll
-            for (int i = 0; i < KN_PER_WAVE; ++i)
-                load_to_lds(Bg + kn_off[i] + (int64_t)k0 * p.ldb, Bs + (wave + NW * i) * 512);
-        } else if (!diag) {
-#pragma unroll
-            for (int i = 0; i < RP_PER_WAVE; ++i)
-                load_to_lds(Bg + rb_off[i] + k0, Bs + (wave + NW * i) * 512);
+        if (d < RP_PER_WAVE) {
+            load_to_lds(Ag + ra_off[d] + k0, smem[st][0] + (wave + NW * d) * 512);
+        } else {
+            const int e = d - RP_PER_WAVE;
+            if (MODE == NS_AXPY)
+                load_to_lds(Bg + kn_off[e] + (int64_t)k0 * p.ldb, smem[st][1] + (wave + NW * e) * 512);
+            else if (!diag)
+                load_to_lds(Bg + rb_off[e] + k0, smem[st][1] + (wave + NW * e) * 512);
         }
     };
 
@@ -198,105 +247,116 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     const int tr_k = 8 * (tg >> 1) + (tix >> 2);          // + kk*16 + 4*h
     const int tr_n = 16 * (tg & 1) + 4 * (tix & 3);       // + wn0 + j*32
 
-    // Fragment loads of one 16-wide K sub-step from an LDS stage into registers.  The
-    // K x N operand's fragments come back as raw 64-bit halves (tr[j][h]) and are only
-    // usable after lds_wait_tied().
-    auto load_frags = [&](const uint16_t* As, const uint16_t* Bs, int kk, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN],
-                          uint2 (&tr)[FN][2]) {
+    // One LDS fragment read (index r of NRD per sub-step) of sub-step kk from stage st:
+    // r < FM are the row-panel fragments af[r]; the rest are the right operand's, either
+    // row-panel fragments bfr[j] or, in NS_AXPY, transposed halves tr[j][h].
+    constexpr int NRD = FM + ((MODE == NS_AXPY) ? 2 * FN : FN);
+    auto rd = [&](int r, int st, int kk, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN], bf16x4 (&tr)[FN][2]) {
         const int c = kk * 2 + khalf;                     // logical 16-byte chunk
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[i] = *reinterpret_cast<const bf16x8*>(As + a_rd[i] + ((c ^ (arow & 7)) << 3));
-        if (MODE == NS_AXPY) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int n = wn0 + j * 32 + tr_n;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int k = kk * 16 + 4 * h + tr_k;
-                    const int g = (n >> 5) ^ (kn_swz(k) % KN_NG);
-                    tr[j][h] = lds_read_tr16(Bs + k * TILE + g * 32 + (n & 31));
-                }
-            }
+        const uint16_t* As = smem[st][0];
+        const uint16_t* Bs = (MODE != NS_AXPY && diag) ? smem[st][0] : smem[st][1];
+        if (r < FM) {
+            af[r] = *reinterpret_cast<const bf16x8*>(As + a_rd[r] + ((c ^ rp_swz(arow)) << 3));
+        } else if (MODE == NS_AXPY) {
+            const int j = (r - FM) >> 1, h = (r - FM) & 1;
+            const int n = wn0 + j * 32 + tr_n;
+            const int k = kk * 16 + 4 * h + tr_k;
+            const int g = (n >> 5) ^ (kn_swz(k) % KN_NG);
+            tr[j][h] = lds_read_tr16(Bs + k * TILE + g * 32 + (n & 31));
         } else {
+            const int j = r - FM;
+            bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + b_rd[j] + ((c ^ rp_swz(arow)) << 3));
+        }
+    };
+    // Assemble the right operand of NS_AXPY from its two transposed halves.
+    auto join_tr = [&](bf16x4 (&tr)[FN][2], bf16x8 (&bfr)[FN]) {
+        if (MODE == NS_AXPY) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + b_rd[j] + ((c ^ (arow & 7)) << 3));
+                bfr[j] = __builtin_shufflevector(tr[j][0], tr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
-    // Wait for every LDS read of this wave, with the transposed halves as in/out operands
-    // so that no MFMA using them can be scheduled before the wait; then assemble them.
-    auto lds_wait_tied = [&](uint2 (&tr)[FN][2], bf16x8 (&bfr)[FN]) {
-        if (MODE == NS_AXPY) {
-            if constexpr (FN == 4) {
-                asm volatile("s_waitcnt lgkmcnt(0)"
-                             : "+v"(tr[0][0]), "+v"(tr[0][1]), "+v"(tr[1][0]), "+v"(tr[1][1]),
-                               "+v"(tr[2][0]), "+v"(tr[2][1]), "+v"(tr[3][0]), "+v"(tr[3][1]));
-            } else if constexpr (FN == 2) {
-                asm volatile("s_waitcnt lgkmcnt(0)"
-                             : "+v"(tr[0][0]), "+v"(tr[0][1]), "+v"(tr[1][0]), "+v"(tr[1][1]));
-            } else {
-                static_assert(FN == 1, "FN");
-                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(tr[0][0]), "+v"(tr[0][1]));
-            }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const uint4 w = make_uint4(tr[j][0].x, tr[j][0].y, tr[j][1].x, tr[j][1].y);
-                bfr[j] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-    };
-    // MFMAs of one sub-step, in two halves (flat index over the FM x FN blocks).
-    constexpr int NMF = FM * FN, HALF = (NMF + 1) / 2;
-    auto mfmas = [&](const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN], int lo, int hi) {
-#pragma unroll
-        for (int f = 0; f < NMF; ++f) {
-            if (f < lo || f >= hi) continue;
-            const int i = f / FN, j = f % FN;
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
-    };
-    auto stage_a = [&](int s) -> const uint16_t* { return smem[s][0]; };
-    auto stage_b = [&](int s) -> const uint16_t* {
-        return (MODE != NS_AXPY && diag) ? smem[s][0] : smem[s][1];
-    };
+
+    // Issue schedule of one sub-step (the order is pinned with scheduling barriers): NMF
+    // MFMAs, each followed by at most RPS fragment reads of the next sub-step and, in the
+    // first sub-step of a K step, DPS direct-to-LDS loads for STAGES - 1 K steps ahead.
+    // In the last sub-step of a K step, the wait for the next stage's loads and the
+    // barrier that publishes it come first; the next stage's reads then fill the last NRS
+    // MFMA slots.
+    constexpr int NMF = FM * FN;
+    constexpr int RPS = (NRD + NMF - 1) / NMF;
+    constexpr int NRS = (NRD + RPS - 1) / RPS;
+    constexpr int DPS = (NDMA + NMF - 1) / NMF;
+    constexpr int AHEAD = STAGES - 1;                     // K steps of loads in flight
+    static_assert(NRS <= NMF, "read slots");
 
     const int nk = p.K / BK;
-    issue_loads(0, 0);
-    wait_vmem();
+    // prologue: fill the first STAGES - 1 stages, wait for stage 0
+#pragma unroll
+    for (int s0 = 0; s0 < AHEAD; ++s0) {
+        if (s0 < nk) {
+#pragma unroll
+            for (int d = 0; d < NDMA; ++d) dma(d, s0, s0);
+        }
+    }
+    // Diagonal tiles of the symmetric products load one panel, so their batches are
+    // RP_PER_WAVE instructions long instead of NDMA.
+    auto wait_next_stage = [&](bool younger_in_flight) {
+        if (!younger_in_flight) wait_vm<0, true>();
+        else if (diag) wait_vm<RP_PER_WAVE * (AHEAD - 1), true>();
+        else wait_vm<NDMA * (AHEAD - 1), true>();
+    };
+    wait_next_stage(nk >= AHEAD);
     __syncthreads();
 
-    // Two register sets of fragments.  Each sub-step issues its first half of MFMAs, then
-    // the LDS reads of the next sub-step, then its second half, so that the reads overlap
-    // MFMA execution and at most one sub-step of reads is outstanding when a wait is due.
-    // The barrier that publishes the next LDS stage sits inside the last sub-step, so the
-    // next stage's first fragments are read while that sub-step's second half executes.
     bf16x8 fa[2][FM], fb[2][FN];
-    uint2 ftr[2][FN][2];
-    load_frags(stage_a(0), stage_b(0), 0, fa[0], fb[0], ftr[0]);
-    lds_wait_tied(ftr[0], fb[0]);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) issue_loads(kt + 1, s ^ 1);
+    bf16x4 ftr[2][FN][2];
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int r = 0; r < NRD; ++r) rd(r, 0, 0, fa[0], fb[0], ftr[0]);
+    join_tr(ftr[0], fb[0]);
+
+    int st = 0;                                           // stage of K step kt
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool issue = kt + AHEAD < nk;               // loads for K step kt + AHEAD
+        const bool more = kt + 1 < nk;
+        const int st_next = (st + 1 == STAGES) ? 0 : st + 1;
+        const int st_load = (st == 0) ? STAGES - 1 : st - 1;  // (kt + AHEAD) % STAGES
+#pragma unroll
+        for (int kk = 0; kk < KSUB; ++kk) {
             const int cur = kk & 1, nxt = cur ^ 1;
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(fa[cur], fb[cur], 0, HALF);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < BK / 16) {
-                load_frags(stage_a(s), stage_b(s), kk + 1, fa[nxt], fb[nxt], ftr[nxt]);
-            } else if (more) {
-                wait_all_mem();
-                __syncthreads();
-                load_frags(stage_a(s ^ 1), stage_b(s ^ 1), 0, fa[nxt], fb[nxt], ftr[nxt]);
+            const bool last = kk + 1 == KSUB;
+            const int rd_lo = last ? NMF - NRS : 0;        // first MFMA slot followed by reads
+#pragma unroll
+            for (int f = 0; f < NMF; ++f) {
+                const int i = f / FN, j = f % FN;
+                __builtin_amdgcn_sched_barrier(0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kk == 0 && issue) {
+#pragma unroll
+                    for (int q = 0; q < DPS; ++q) {
+                        const int d = f * DPS + q;
+                        if (d < NDMA) dma(d, kt + AHEAD, st_load);
+                    }
+                }
+                if (last && f == rd_lo && more) {
+                    // the next stage's loads were issued AHEAD - 1 K steps ago; let the
+                    // younger batches stay in flight
+                    wait_next_stage(issue);
+                    __syncthreads();
+                }
+                if (f >= rd_lo && f < rd_lo + NRS && (!last || more)) {
+#pragma unroll
+                    for (int q = 0; q < RPS; ++q) {
+                        const int r = (f - rd_lo) * RPS + q;
+                        if (r < NRD) rd(r, last ? st_next : st, last ? 0 : kk + 1, fa[nxt], fb[nxt], ftr[nxt]);
+                    }
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(fa[cur], fb[cur], HALF, NMF);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kk + 1 < BK / 16 || more) lds_wait_tied(ftr[nxt], fb[nxt]);
+            if (!last || more) join_tr(ftr[nxt], fb[nxt]);
         }
+        st = st_next;
     }
 
     // ---- epilogue ---------------------------------------------------------------------
@@ -312,11 +372,11 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     constexpr int EP_ROWS_PER_INSTR = 512 / TILE;
     constexpr int EP_INSTR = TILE / EP_ROWS_PER_INSTR;
     constexpr int EP_PER_WAVE = EP_INSTR / NW;
-    uint16_t* Es = &smem[0][0][0];                        // TILE x TILE bf16 fits in the two stages
+    uint16_t* Es = &smem[0][0][0];                        // TILE x TILE bf16 fits in the stages
     if (MODE == NS_POLY || MODE == NS_AXPY) {
         const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
         // every wave must be done reading the K stages before they are overwritten
-        wait_all_mem();
+        wait_vm<0, true>();
         __syncthreads();
 #pragma unroll 4
         for (int i = 0; i < EP_PER_WAVE; ++i) {
@@ -326,7 +386,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
             const int g = (pc >> 2) ^ (ep_swz(r) % KN_NG);
             load_to_lds(Eg + (int64_t)r * p.ldo + (g * 4 + (pc & 3)) * 8, Es + q * 512);
         }
-        wait_vmem();
+        wait_vm<0, true>();
         __syncthreads();
     }
     const int col_in = lane & 31, rsub = (lane >> 5) * 4;
@@ -335,7 +395,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int gc = tj * TILE + wn0 + j * 32 + col_in;
-            uint2 e[4];
+            bf16x4 e[4];
             if (MODE == NS_POLY || MODE == NS_AXPY) {
                 const int c = wn0 + j * 32 + tr_n;        // supplying-lane column block
 #pragma unroll
@@ -344,7 +404,6 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
                     const int g = (c >> 5) ^ (ep_swz(r) % KN_NG);
                     e[q] = lds_read_tr16(Es + r * TILE + g * 32 + (c & 31));
                 }
-                asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]));
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -353,11 +412,8 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     float val = acc[i][j][q * 4 + v];
-                    if (MODE == NS_POLY || MODE == NS_AXPY) {
-                        const uint32_t w = (v < 2) ? e[q].x : e[q].y;
-                        const uint32_t hv = (v & 1) ? (w >> 16) : (w & 0xffffu);
-                        val = p.alpha * dev::bf16_to_f32(hv) + p.gamma * val;
-                    }
+                    if (MODE == NS_POLY || MODE == NS_AXPY)
+                        val = p.alpha * (float)e[q][v] + p.gamma * val;
                     h[v] = dev::f32_to_bf16(val);
                     out[(int64_t)(gr0 + v) * p.ldo + gc] = h[v];
                 }
@@ -372,9 +428,9 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     }
 }
 
-template <int MODE, int TILE, int WM, int WN>
+template <int MODE, int TILE, int WM, int WN, int BK, int STAGES>
 hipError_t launch_cfg(const NsArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((ns_gemm_kernel<MODE, TILE, WM, WN>), dim3((unsigned)a.total_tiles),
+    hipLaunchKernelGGL((ns_gemm_kernel<MODE, TILE, WM, WN, BK, STAGES>), dim3((unsigned)a.total_tiles),
                        dim3(64 * WM * WN), 0, s, a);
     return hipGetLastError();
 }
@@ -382,9 +438,9 @@ hipError_t launch_cfg(const NsArgs& a, hipStream_t s) {
 template <int MODE>
 hipError_t launch_mode(int32_t tile, const NsArgs& a, hipStream_t s) {
     switch (tile) {
-        case TILE_256: return launch_cfg<MODE, 256, 2, 2>(a, s);
-        case TILE_128: return launch_cfg<MODE, 128, 2, 2>(a, s);
-        case TILE_64: return launch_cfg<MODE, 64, 2, 2>(a, s);
+        case TILE_256: return launch_cfg<MODE, 256, 2, 4, 64, 2>(a, s);
+        case TILE_128: return launch_cfg<MODE, 128, 2, 2, 64, 2>(a, s);
+        case TILE_64: return launch_cfg<MODE, 64, 2, 2, 64, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
