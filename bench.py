@@ -5,13 +5,15 @@
 A step is the whole hot path over every 2-D matrix of the workload: momentum update +
 bf16 cast, Frobenius normalisation, k quintic Newton–Schulz iterations (SYRK, SYRK+poly,
 GEMM+axpy per iteration), and the float32 apply with decoupled weight decay — all in
-libmuon's HIP kernels, with inputs resident in HBM.  W untimed steps run first; then K
-steps are timed between device synchronisations.  Prints one JSON line.
+libmuon's HIP kernels, with inputs resident in HBM.  W untimed steps run first (the first
+eagerly, the rest as replays of the captured step graph); then K graph replays are timed
+between device synchronisations.  Prints one JSON line.
 
   value        effective NS TFLOP/s over the whole step: conventional Newton–Schulz FLOPs
                (4 m^2 n + 2 m^3 per iteration and matrix) / step time
   roofline     the kernel that takes the most time, from HIP events recorded around each
-               of its launches on its own stream during the timed steps: algorithmic
+               of its launches on its own stream during K further steps launched kernel
+               by kernel (a graph replay hides its kernels from events): algorithmic
                FLOPs (or bytes) per launch / mean launch time, against MI355X's published
                peak (bf16 dense MFMA 2.5 PFLOP/s; HBM 8 TB/s)
   cpu_baseline the float64 CPU oracle (test infrastructure, untuned) on a bounded sample
@@ -124,26 +126,45 @@ def main(argv=None):
     def step():
         plan.step(w.beta, w.lr, w.wd, w.a, w.b, w.c, w.steps, w.eps)
 
-    # first warm-up step: its outputs are the sampled parity check
+    # first warm-up step (eager): its outputs are the sampled parity check
     step()
     torch.cuda.synchronize()
     first = {}
     for i in snap:
         first[i] = (plan.output_oriented(i).float().cpu().numpy().astype(np.float64),
                     params[i].momentum.cpu().numpy(), params[i].weight.cpu().numpy())
+
+    # the step as one graph; the remaining warm-up steps are replays of it
+    graph = plan.capture(w.beta, w.lr, w.wd, w.a, w.b, w.c, w.steps, w.eps)
     for _ in range(args.warmup - 1):
-        step()
+        graph.launch(stream)
     torch.cuda.synchronize()
 
-    launches_per_step = sum(3 + 3 * w.steps + 1 for _ in range(plan.n_chunks)) + 2
-    plan.timing_enable(launches_per_step * args.steps + 16)
+    # ---- timed region: K graph replays, between device synchronisations ---------------
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for e0, e1 in ev:
+        e0.record(stream)
+        graph.launch(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
+    replay_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    graph_nodes = graph.nodes
+    graph.close()
+
+    # ---- kernel timing: K more steps launched one kernel at a time, each kernel between
+    # a HIP event pair recorded on its own launch stream --------------------------------
+    launches_per_step = plan.n_chunks * (4 + 3 * w.steps)
+    plan.timing_enable(launches_per_step * args.steps + 16)
+    torch.cuda.synchronize()
+    t_eager = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t_eager) * 1e3 / args.steps
 
     kernels = {}
     for k in range(L.MUON_KERNEL_COUNT):
@@ -168,6 +189,7 @@ def main(argv=None):
         "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
         "frac": round(dk["frac"], 4), "traffic": load_traffic(dom, w.key),
         "work_per_launch": dk["work_per_launch"], "mean_launch_ms": dk["mean_launch_ms"],
+        "measured_over": f"{args.steps} steps launched kernel by kernel right after the timed graph replays",
     }
 
     conv, alg = w.ns_flops()
@@ -237,6 +259,11 @@ def main(argv=None):
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "graph": {
+            "nodes": graph_nodes, "replay_ms_median": round(replay_ms[len(replay_ms) // 2], 4),
+            "replay_ms_min": round(replay_ms[0], 4),
+            "eager_ms_per_step": round(eager_ms, 4),
+        },
         "ns": {
             "ms_per_step": round(ns_ms, 4),
             "effective_tflops_conventional": round(conv / (ns_ms * 1e-3) / 1e12, 2),

@@ -188,6 +188,34 @@ MUON_API muon_status muon_apply(const muon_plan* plan, int32_t chunk, float lr, 
 MUON_API muon_status muon_step(const muon_plan* plan, int32_t chunk, float beta, float a, float b,
                       float c, int32_t steps, float eps, float lr, float wd, void* stream);
 
+/* ---- the whole step as one graph ------------------------------------------------------- */
+
+/* The pages count kernel-dispatch overhead among the causes of the gap between the
+ * measured optimizer step and its communication limit ("Frontier Pre-training at
+ * Microsoft AI", method details section 5, "Scaling Muon to 16K GPUs", overhead
+ * analysis; the same list in "MAI-Base-2 в 4–12 раз экономнее DeepSeek на
+ * предобучении", its optimizer section).
+ * A step issues 2 + 3*steps + 2 launches per chunk; as a graph it is one launch.
+ *
+ * muon_graph_capture records muon_step(plan, -1, ...) on a private stream into a HIP
+ * graph and instantiates it.  Nothing runs during capture.  The graph holds the device
+ * addresses of W, M, G and of the workspace bound at capture time, and the scalars
+ * given here: a later muon_plan_bind does not move it, and the caller keeps all of
+ * those buffers alive and in place while the graph exists.  New gradients are picked
+ * up by writing them into the same G buffers before each launch.  Kernel timing is not
+ * recorded inside graphs.  Errors: INVALID_ARG, NOT_BOUND, HIP (capture or
+ * instantiation failed; nothing is left allocated). */
+typedef struct muon_graph muon_graph;
+MUON_API muon_status muon_graph_capture(const muon_plan* plan, float beta, float a, float b, float c,
+                               int32_t steps, float eps, float lr, float wd, muon_graph** out);
+/* Launch one step, ordered on `stream` (the null stream is allowed).  Launches of one
+ * graph, or of graphs of one plan, must not overlap on different streams. */
+MUON_API muon_status muon_graph_launch(const muon_graph* graph, void* stream);
+/* Number of nodes in the captured graph (one per kernel launch). */
+MUON_API muon_status muon_graph_node_count(const muon_graph* graph, int64_t* nodes);
+/* Free the graph; the caller makes sure no launch of it is still running. */
+MUON_API void muon_graph_destroy(muon_graph* graph);
+
 /* ---- per-kernel timing (HIP events on the launching stream) --------------------------- */
 
 #define MUON_KERNEL_MOMENTUM 0

@@ -98,6 +98,13 @@ muon_apply = _fn("muon_apply", C.c_int32, [_P, C.c_int32, C.c_float, C.c_float, 
 muon_step = _fn("muon_step", C.c_int32,
                 [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float,
                  C.c_float, C.c_float, C.c_void_p])
+_G = C.c_void_p  # muon_graph*
+muon_graph_capture = _fn("muon_graph_capture", C.c_int32,
+                         [_P, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float, C.c_float,
+                          C.c_float, C.POINTER(_G)])
+muon_graph_launch = _fn("muon_graph_launch", C.c_int32, [_G, C.c_void_p])
+muon_graph_node_count = _fn("muon_graph_node_count", C.c_int32, [_G, C.POINTER(C.c_int64)])
+muon_graph_destroy = _fn("muon_graph_destroy", None, [_G])
 muon_timing_enable = _fn("muon_timing_enable", C.c_int32, [_P, C.c_int32])
 muon_timing_read = _fn("muon_timing_read", C.c_int32,
                        [_P, C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int64), C.POINTER(C.c_double)])
@@ -110,7 +117,8 @@ muon_last_error = _fn("muon_last_error", C.c_char_p, [])
 EXPORTED = [
     "muon_plan_buckets", "muon_plan_workspace_bytes", "muon_plan_counts", "muon_plan_info",
     "muon_plan_param_info", "muon_plan_validate", "muon_plan_bind", "muon_momentum_update",
-    "muon_ns_batched", "muon_apply", "muon_step", "muon_timing_enable", "muon_timing_read",
+    "muon_ns_batched", "muon_apply", "muon_step", "muon_graph_capture", "muon_graph_launch",
+    "muon_graph_node_count", "muon_graph_destroy", "muon_timing_enable", "muon_timing_read",
     "muon_timing_reset", "muon_kernel_name", "muon_plan_destroy", "muon_status_string",
     "muon_last_error",
 ]

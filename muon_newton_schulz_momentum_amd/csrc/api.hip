@@ -36,13 +36,17 @@ muon_status check_step(const muon_plan* p, int32_t chunk, const char* who) {
 
 // ---- per-launch timing ------------------------------------------------------------------
 
+// Set while this thread records a step into a graph: launches then carry no event pairs,
+// since an event recorded inside a graph would be overwritten by every replay.
+thread_local bool t_capturing = false;
+
 struct TimedLaunch {
     muon_plan* p;
     int slot = -1;
     TimedLaunch(const muon_plan* plan, int32_t kind, double work, hipStream_t s)
         : p(const_cast<muon_plan*>(plan)) {
         TimingState& t = p->timing;
-        if (t.used >= t.capacity) return;
+        if (t_capturing || t.used >= t.capacity) return;
         slot = t.used++;
         t.kind[slot] = kind;
         t.work[slot] = work;
@@ -168,6 +172,28 @@ muon_status apply_chunk(const muon_plan* p, const Chunk& c, float lr, float wd, 
 
 bool finite(float v) { return std::isfinite(v); }
 
+// Steps 1, 3 and 5 for one chunk (-1 = every chunk, in order) on one stream.
+muon_status step_chunks(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,
+                        float eps, float lr, float wd, hipStream_t s) {
+    muon_status st;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        if (chunk != -1 && i != chunk) continue;
+        const Chunk& ch = p->chunks[(size_t)i];
+        if ((st = momentum_chunk(p, ch, beta, s)) != MUON_OK) return st;
+        if ((st = ns_chunk(p, ch, a, b, c, steps, eps, s)) != MUON_OK) return st;
+        if ((st = apply_chunk(p, ch, lr, wd, s)) != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
+muon_status check_step_scalars(float beta, float a, float b, float c, int32_t steps, float eps, float lr, float wd,
+                               const char* who) {
+    if (!finite(beta) || !finite(lr) || !finite(wd) || !finite(a) || !finite(b) || !finite(c) || !finite(eps) ||
+        eps < 0.f || steps < 1)
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": scalars must be finite, eps >= 0 and steps >= 1");
+    return MUON_OK;
+}
+
 // The tile grid of a chunk must fit the kernels' int32 indexing.
 bool grid_fits(const Chunk& c) {
     const int64_t tm = c.mp / c.tile, tn = c.np / c.tile;
@@ -260,19 +286,83 @@ muon_status muon_step(const muon_plan* p, int32_t chunk, float beta, float a, fl
     if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_step: call muon_plan_bind first");
     if (chunk < -1 || chunk >= (int32_t)p->chunks.size())
         return set_error(MUON_ERR_INVALID_ARG, "muon_step: chunk out of range");
-    if (!finite(beta) || !finite(lr) || !finite(wd) || !finite(a) || !finite(b) || !finite(c) || !finite(eps) ||
-        eps < 0.f || steps < 1)
-        return set_error(MUON_ERR_INVALID_ARG, "muon_step: scalars must be finite, eps >= 0 and steps >= 1");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    muon_status st;
-    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
-        if (chunk != -1 && i != chunk) continue;
-        const Chunk& ch = p->chunks[(size_t)i];
-        if ((st = momentum_chunk(p, ch, beta, s)) != MUON_OK) return st;
-        if ((st = ns_chunk(p, ch, a, b, c, steps, eps, s)) != MUON_OK) return st;
-        if ((st = apply_chunk(p, ch, lr, wd, s)) != MUON_OK) return st;
+    muon_status st = check_step_scalars(beta, a, b, c, steps, eps, lr, wd, "muon_step");
+    if (st != MUON_OK) return st;
+    return step_chunks(p, chunk, beta, a, b, c, steps, eps, lr, wd, static_cast<hipStream_t>(stream));
+}
+
+// ---- the step as one graph ----------------------------------------------------------------
+
+muon_status muon_graph_capture(const muon_plan* p, float beta, float a, float b, float c, int32_t steps, float eps,
+                               float lr, float wd, muon_graph** out) {
+    clear_error();
+    if (!out) return set_error(MUON_ERR_INVALID_ARG, "muon_graph_capture: out is NULL");
+    *out = nullptr;
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_graph_capture: plan is NULL");
+    if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_graph_capture: call muon_plan_bind first");
+    muon_status st = check_step_scalars(beta, a, b, c, steps, eps, lr, wd, "muon_graph_capture");
+    if (st != MUON_OK) return st;
+
+    // A private stream: the caller's stream may be the null stream, which cannot capture.
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "muon_graph_capture: hipStreamCreateWithFlags");
+    hipGraph_t graph = nullptr;
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return hip_fail(e, "muon_graph_capture: hipStreamBeginCapture");
     }
+    t_capturing = true;
+    st = step_chunks(p, -1, beta, a, b, c, steps, eps, lr, wd, cs);
+    t_capturing = false;
+    const std::string launch_error = st == MUON_OK ? std::string() : std::string(muon_last_error());
+    e = hipStreamEndCapture(cs, &graph);
+    (void)hipStreamDestroy(cs);
+    if (st != MUON_OK) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return set_error(st, "muon_graph_capture: " + launch_error);
+    }
+    if (e != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return hip_fail(e, "muon_graph_capture: hipStreamEndCapture");
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        return hip_fail(e, "muon_graph_capture: hipGraphInstantiate");
+    }
+    size_t nodes = 0;
+    (void)hipGraphGetNodes(graph, nullptr, &nodes);
+    muon_graph* g = new muon_graph;
+    g->graph = graph;
+    g->exec = exec;
+    g->nodes = (int64_t)nodes;
+    g->ws = p->ws;
+    *out = g;
     return MUON_OK;
+}
+
+muon_status muon_graph_launch(const muon_graph* g, void* stream) {
+    clear_error();
+    if (!g) return set_error(MUON_ERR_INVALID_ARG, "muon_graph_launch: graph is NULL");
+    const hipError_t e = hipGraphLaunch((hipGraphExec_t)g->exec, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "muon_graph_launch: hipGraphLaunch");
+}
+
+muon_status muon_graph_node_count(const muon_graph* g, int64_t* nodes) {
+    clear_error();
+    if (!g || !nodes) return set_error(MUON_ERR_INVALID_ARG, "muon_graph_node_count: bad argument");
+    *nodes = g->nodes;
+    return MUON_OK;
+}
+
+void muon_graph_destroy(muon_graph* g) {
+    if (!g) return;
+    (void)hipGraphExecDestroy((hipGraphExec_t)g->exec);
+    (void)hipGraphDestroy((hipGraph_t)g->graph);
+    delete g;
 }
 
 muon_status muon_timing_enable(muon_plan* p, int32_t capacity) {

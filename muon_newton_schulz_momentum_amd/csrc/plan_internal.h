@@ -83,6 +83,15 @@ struct muon_plan {
     muon::TimingState timing;
 };
 
+// An instantiated graph of one whole step.  It holds the device addresses of the
+// workspace it was captured against, not the host plan.
+struct muon_graph {
+    void* graph = nullptr;   // hipGraph_t
+    void* exec = nullptr;    // hipGraphExec_t
+    int64_t nodes = 0;
+    void* ws = nullptr;
+};
+
 namespace muon {
 
 // Thread-local error message shared by both translation units.

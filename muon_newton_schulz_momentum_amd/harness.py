@@ -122,6 +122,14 @@ class Plan:
         L.check(L.muon_step(self._plan, chunk, beta, a, b, c, steps, eps, lr, wd, _stream_ptr(stream)),
                 "muon_step")
 
+    def capture(self, beta, lr, wd, a=wl.NS_A, b=wl.NS_B, c=wl.NS_C, steps=wl.NS_STEPS,
+                eps=wl.NS_EPS) -> "Graph":
+        """The whole step (every chunk) as one replayable graph, tied to this workspace."""
+        g = C.c_void_p()
+        L.check(L.muon_graph_capture(self._plan, beta, a, b, c, steps, eps, lr, wd, C.byref(g)),
+                "muon_graph_capture")
+        return Graph(g, self)
+
     # ---- queries -----------------------------------------------------------------------
     def chunk_info(self, chunk: int) -> L.muon_chunk_info:
         info = L.muon_chunk_info()
@@ -165,6 +173,31 @@ class Plan:
         L.check(L.muon_timing_read(self._plan, kernel, C.byref(ms), C.byref(n), C.byref(work)),
                 "muon_timing_read")
         return float(ms.value), int(n.value), float(work.value)
+
+
+class Graph:
+    """An instantiated graph of one step; keeps its plan (and so the workspace) alive."""
+
+    def __init__(self, handle: C.c_void_p, plan: Plan):
+        self._g = handle
+        self.plan = plan
+        n = C.c_int64()
+        L.check(L.muon_graph_node_count(self._g, C.byref(n)), "muon_graph_node_count")
+        self.nodes = int(n.value)
+
+    def launch(self, stream=None):
+        L.check(L.muon_graph_launch(self._g, _stream_ptr(stream)), "muon_graph_launch")
+
+    def close(self):
+        if self._g:
+            L.muon_graph_destroy(self._g)
+            self._g = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def make_params(w: wl.Workload, device="cuda", indices: Optional[Sequence[int]] = None) -> List[ParamTensors]:

@@ -38,6 +38,7 @@ __all__ = [
     "bf16_round",
     "momentum_update",
     "canonical_orientation",
+    "ns_iteration_rows",
     "frobenius_normalise",
     "ns_iterate",
     "newton_schulz",
@@ -147,6 +148,27 @@ def ns_iterate(X, a, b, c, steps, emulate_bf16=True):
         B = R(b * A + c * (A @ A))
         X = R(a * X + B @ X)
     return X
+
+
+def ns_iteration_rows(X, a, b, c, rows, emulate_bf16=True):
+    """Selected rows of ONE Newton–Schulz step applied to X (m x n, m <= n expected).
+
+    The same step as ns_iterate (A = X X^T, B = b A + c A A, X' = a X + B X, with the
+    same cast points), evaluated only where it is needed for the requested rows of X':
+    A in full (B's rows need all of A), then B's rows as b A[r] + c A[r] A, then
+    X'[r] = a X[r] + B[r] X.  Row r of each product is the matching row of the full
+    product, so the result equals ns_iterate(X, ..., steps=1)[rows].  Used to check an
+    iteration of a matrix too large for the whole oracle chain, one iteration at a time.
+    """
+    R = bf16_round if emulate_bf16 else (lambda v: v)
+    a = f32(a)[()]
+    b = f32(b)[()]
+    c = f32(c)[()]
+    X = np.asarray(X, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    A = R(X @ X.T)
+    Br = R(b * A[rows] + c * (A[rows] @ A))
+    return R(a * X[rows] + Br @ X)
 
 
 def newton_schulz(X0, a, b, c, steps, eps, emulate_bf16=True):

@@ -253,6 +253,14 @@ def test_step_calls_refused_before_bind_and_bind_checks():
     assert L.muon_ns_batched(p, 0, 3.4445, -4.775, 2.0315, 5, 1e-7, None) == L.MUON_ERR_NOT_BOUND
     assert L.muon_apply(p, 0, 0.02, 0.1, None) == L.MUON_ERR_NOT_BOUND
     assert L.muon_step(p, -1, 0.95, 3.4, -4.7, 2.0, 5, 1e-7, 0.02, 0.1, None) == L.MUON_ERR_NOT_BOUND
+    g = C.c_void_p(1)
+    assert L.muon_graph_capture(p, 0.95, 3.4, -4.7, 2.0, 5, 1e-7, 0.02, 0.1, C.byref(g)) == L.MUON_ERR_NOT_BOUND
+    assert not g.value    # *out is cleared on every error
+    assert L.muon_graph_capture(p, 0.95, 3.4, -4.7, 2.0, 5, 1e-7, 0.02, 0.1, None) == L.MUON_ERR_INVALID_ARG
+    assert L.muon_graph_capture(None, 0.95, 3.4, -4.7, 2.0, 5, 1e-7, 0.02, 0.1, C.byref(g)) \
+        == L.MUON_ERR_INVALID_ARG
+    assert L.muon_graph_launch(None, None) == L.MUON_ERR_INVALID_ARG
+    L.muon_graph_destroy(None)
     assert L.muon_plan_bind(p, None, 1 << 30, None) == L.MUON_ERR_INVALID_ARG
     assert L.muon_plan_bind(p, 1 << 40 | 16, 1 << 30, None) == L.MUON_ERR_ALIGNMENT
     assert L.muon_plan_bind(p, 1 << 40, 16, None) == L.MUON_ERR_WORKSPACE_TOO_SMALL

@@ -375,6 +375,36 @@ def test_ns_iterate_bf16_bruteforce_rational():
     np.testing.assert_array_equal(got, want)
 
 
+def test_ns_iteration_rows_bf16_bruteforce_rational():
+    # one step on a tiny exact input, rows picked out of order and repeated
+    rng = np.random.default_rng(23)
+    X = orc.bf16_round(rng.integers(-40, 41, (4, 6)).astype(np.float64) / 64.0)
+    a, b, c = (Fraction(float(np.float32(v))) for v in (A, B, C))
+    Xr = _frac_mat(X)
+    Ar = _rb(_mm(Xr, [list(r) for r in zip(*Xr)]))
+    AA = _mm(Ar, Ar)
+    Br = _rb([[b * Ar[i][j] + c * AA[i][j] for j in range(4)] for i in range(4)])
+    BX = _mm(Br, Xr)
+    X1 = _rb([[a * Xr[i][j] + BX[i][j] for j in range(6)] for i in range(4)])
+    rows = [3, 0, 3]
+    got = orc.ns_iteration_rows(X, A, B, C, rows, emulate_bf16=True)
+    want = np.array([[float(v) for v in X1[r]] for r in rows])
+    np.testing.assert_array_equal(got, want)
+
+
+def test_ns_iteration_rows_exact_mode_is_svd_polynomial():
+    # exact mode: one step maps X = U S V^T to U p(S) V^T, p(s) = a s + b s^3 + c s^5
+    rng = np.random.default_rng(24)
+    X = rng.standard_normal((20, 33))
+    X /= np.linalg.norm(X)
+    U, S, Vt = np.linalg.svd(X, full_matrices=False)
+    a, b, c = (float(np.float32(v)) for v in (A, B, C))
+    P = (U * (a * S + b * S ** 3 + c * S ** 5)) @ Vt
+    rows = [0, 7, 19, 4]
+    got = orc.ns_iteration_rows(X, A, B, C, rows, emulate_bf16=False)
+    np.testing.assert_allclose(got, P[rows], rtol=0, atol=1e-12)
+
+
 def test_normalise_rounds_scaled_values_once():
     X0 = orc.bf16_round(np.random.default_rng(18).standard_normal((4, 6)))
     X = orc.frobenius_normalise(X0, EPS)
