@@ -153,7 +153,9 @@ MUON_API muon_status muon_plan_validate(const muon_plan* plan, const muon_param_
 
 /* Attach a caller-owned device workspace (>= muon_plan_workspace_bytes, 256-B aligned)
  * and upload the plan's tables, ordered on `stream`.  Also zero-fills the workspace.
- * May be called again with another workspace. */
+ * May be called again with another workspace.  Errors: INVALID_ARG, ALIGNMENT,
+ * WORKSPACE_TOO_SMALL, SHAPE (a chunk needs 2^31 or more tiles, or one padded matrix
+ * takes 2 GiB or more: about 32768 x 32768), HIP. */
 MUON_API muon_status muon_plan_bind(muon_plan* plan, void* workspace, uint64_t bytes, void* stream);
 
 /* ---- the step (device, asynchronous on `stream`) --------------------------------------- */

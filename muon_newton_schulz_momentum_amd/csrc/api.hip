@@ -194,10 +194,13 @@ muon_status check_step_scalars(float beta, float a, float b, float c, int32_t st
     return MUON_OK;
 }
 
-// The tile grid of a chunk must fit the kernels' int32 indexing.
+// The tile grid of a chunk must fit the kernels' int32 indexing, and one padded matrix
+// (X, A or B) the 32-bit byte offsets of the buffer loads.
 bool grid_fits(const Chunk& c) {
     const int64_t tm = c.mp / c.tile, tn = c.np / c.tile;
-    return c.count * tm * tn < (int64_t(1) << 31) && c.count * tm * (tm + 1) / 2 < (int64_t(1) << 31);
+    const int64_t lim = int64_t(1) << 31;
+    return c.count * tm * tn < lim && c.count * tm * (tm + 1) / 2 < lim && c.mp * c.np * 2 < lim &&
+           c.mp * c.mp * 2 < lim;
 }
 
 }  // namespace
@@ -219,7 +222,7 @@ muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream)
         return set_error(MUON_ERR_WORKSPACE_TOO_SMALL, "muon_plan_bind: workspace holds " + std::to_string(bytes) +
                                                            " bytes; the plan needs " + std::to_string(p->ws_bytes));
     for (const Chunk& c : p->chunks)
-        if (!grid_fits(c)) return set_error(MUON_ERR_SHAPE, "muon_plan_bind: chunk tile grid exceeds 2^31 tiles");
+        if (!grid_fits(c)) return set_error(MUON_ERR_SHAPE, "muon_plan_bind: chunk tile grid exceeds 2^31 tiles or a padded matrix exceeds 2 GiB");
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemsetAsync(ws, 0, p->ws_bytes, s);
     if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipMemsetAsync");

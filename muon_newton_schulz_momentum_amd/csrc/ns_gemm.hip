@@ -12,24 +12,28 @@
 //              upper-triangle scheme applies; b A is added in the epilogue.
 //   * NS_AXPY  X' = a X + B X: a full GEMM with the axpy fused into its epilogue.
 //
-// Main loop (all three modes): one TILE x TILE output tile per workgroup, K in steps of
-// BK through a ring of STAGES LDS buffers.  Operand tiles go from global memory straight
-// into LDS with global_load_lds_dwordx4 (no VGPR staging): each lane's 16 bytes land at
-// the instruction's LDS base + 16 * lane, and the lane picks which global 16 bytes to
-// fetch, so the LDS image can be XOR-swizzled for conflict-free reads.  Loads run
-// STAGES - 1 K steps ahead of the v_mfma_f32_32x32x16_bf16 that consume them (256 x 256
-// tiles: 2 stages of BK = 64, 128 KB; measured faster on gfx950 than 4 stages of BK = 32,
-// whose extra barriers cost more than the deeper prefetch saves).
-//   * Row-panel operands (K contiguous: X in SYRK, A in POLY, B in AXPY) are stored as
-//     rows of BK bf16 whose 16-byte chunks are permuted per row so that the 16 lanes the
-//     LDS serves together (64 banks, one ds_read_b128 each) never share a bank.  An MFMA
-//     operand is one ds_read_b128 per lane.
+// Two kernels share the tile order, the fragment layouts and the epilogue:
+//   * ns_vs_kernel (256 x 256 tiles, the large buckets): 4 waves of 128 x 128, one wave
+//     per SIMD with 256 accumulator registers each.  Operand tiles go global -> VGPR
+//     (buffer loads) -> LDS, one K step ahead of the LDS stage being multiplied; on
+//     gfx950 this path keeps more requests in flight than the direct-to-LDS loads when
+//     operands miss in L2 (measured 20-30 % more bytes per CU from the Infinity Cache).
+//   * ns_gemm_kernel (128 and 64 tiles, the small buckets): operand tiles go from global
+//     memory straight into LDS with global_load_lds_dwordx4 (no VGPR staging): each
+//     lane's 16 bytes land at the instruction's LDS base + 16 * lane, and the lane picks
+//     which global 16 bytes to fetch, so the LDS image can be XOR-swizzled.  Loads run
+//     STAGES - 1 K steps ahead of the v_mfma_f32_32x32x16_bf16 that consume them.
+// Common to both:
+//   * Row-panel operands (K contiguous: X in SYRK, A in POLY, B in AXPY) are stored so
+//     that the 16 lanes the LDS serves together (64 banks, one ds_read_b128 each) never
+//     share a bank.  An MFMA operand is one ds_read_b128 per lane.
 //   * The K x N operand of NS_AXPY (X, N contiguous) is stored as rows of TILE bf16 in its
 //     own orientation, with 64-byte granules permuted per row, and read with
 //     ds_read_b64_tr_b16, which transposes 4 x 4 blocks of 16-bit values across each group
 //     of 16 lanes into exactly the K-packed layout the MFMA wants.
-//   * Each MFMA is followed by at most one LDS read or load instruction (the issue order
-//     is pinned with scheduling barriers), so those issue while the matrix pipe is busy.
+//   * Each MFMA is followed by at most a few LDS reads, LDS writes or loads (the issue
+//     order is pinned with scheduling barriers), so those issue while the matrix pipe is
+//     busy.
 //
 // Matrices are padded to multiples of TILE with zero rows and columns, so no kernel
 // needs a bounds check: zero padding stays zero through all three products.
@@ -37,6 +41,8 @@
 // Workgroups are remapped so that the tiles of one matrix run on the same XCD (the
 // hardware hands consecutive workgroup ids to the 8 XCDs in turn), keeping a matrix's
 // panels in that XCD's L2, and tiles are ordered in groups that share operand panels.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -428,6 +434,267 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     }
 }
 
+// ---- 256 x 256 tiles, 4 waves of 128 x 128, operands staged through VGPRs --------------
+//
+// LDS layout (bytes).  Row panels (K contiguous in memory) are stored as 4 K-planes of 16
+// elements: row r, K chunk c (16 bytes, c = 0..7) lands at plane c/2, offset r*32 plus
+// 16 * ((c & 1) ^ ((r >> 3) & 1)); planes are 8192 + 64 bytes apart, so consecutive planes
+// start 64 bytes further round the 64 banks.  Every fragment read and every staging write
+// is then one per-lane base register plus a compile-time offset (plane, fragment, stage),
+// and the 16 lanes the LDS serves together touch 16 different 16-byte bank groups, for
+// reads (16 rows, one chunk) as well as for writes (2 rows, 8 chunks).  The K x N panel of
+// the axpy keeps the 512-byte rows with permuted 64-byte granules of ns_gemm_kernel.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t elems) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(elems * 2), 0x00020000);
+}
+
+__device__ __forceinline__ void lds_wait_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void ns_vs_kernel(NsArgs p) {
+    constexpr int TILE = 256, BK = 64, NW = 4, WTM = 128, WTN = 128, FM = 4, FN = 4;
+    constexpr int KSUB = BK / 16;
+    constexpr int NCH = 8;                            // 16-byte chunks per thread and operand
+    constexpr int KN_NG = TILE / 32;
+    constexpr int PLANE_B = 8192 + 64;
+    constexpr int RP_B = 4 * PLANE_B;                 // one row panel (256 x 64 bf16)
+    constexpr int KN_B = 64 * TILE * 2;               // one K x N panel (64 x 256 bf16)
+    constexpr int OFF_B = 2 * RP_B;                   // second operand's stages
+    constexpr int B_STAGE = (MODE == NS_AXPY) ? KN_B : RP_B;
+    constexpr int SMEM = OFF_B + 2 * B_STAGE;
+    static_assert(SMEM >= TILE * TILE * 2, "epilogue tile fits");
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave >> 1) * WTM, wn0 = (wave & 1) * WTN;
+
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int mat = b / p.tiles_per_mat;
+    const int t = b - mat * p.tiles_per_mat;
+    int ti, tj;
+    if (MODE == NS_AXPY) grid_decode(t, p.tiles_m, p.tiles_n, ti, tj);
+    else tri_decode(t, p.tiles_m, ti, tj);
+    const bool diag = MODE != NS_AXPY && ti == tj;
+
+    // buffer resources from the first element of each operand panel to the end of its matrix
+    const int64_t a0 = (int64_t)ti * TILE * p.lda;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.opa + (int64_t)mat * p.stride_a + a0, p.stride_a - a0);
+    const int64_t b0 = (MODE == NS_AXPY) ? (int64_t)tj * TILE : (int64_t)tj * TILE * p.ldb;
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.opb + (int64_t)mat * p.stride_b + b0, p.stride_b - b0);
+
+    // staging: row panels -> rows row0 + 32 i, chunk ch; K x N -> rows klo + 8 i, chunk nc
+    const int row0 = tid >> 3, ch = tid & 7;
+    const int va = row0 * p.lda * 2 + ch * 16;
+    const int vb_rp = row0 * p.ldb * 2 + ch * 16;
+    const int klo = tid >> 5, nc = tid & 31;
+    const int vb_kn = klo * p.ldb * 2 + nc * 16;
+    const int w_rp = (ch >> 1) * PLANE_B + row0 * 32 + (((ch & 1) ^ ((row0 >> 3) & 1)) << 4);
+    int w_kn[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int swz = (klo & 3) | (4 * par);
+        w_kn[par] = OFF_B + klo * TILE * 2 + (((((nc >> 2) ^ (swz % KN_NG)) << 2) | (nc & 3)) << 4);
+    }
+
+    i32x4 sa[NCH], sb[NCH];
+    auto gload_a = [&](int i, int kt) {
+        sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, kt * BK * 2 + i * 32 * p.lda * 2, 0);
+    };
+    auto gload_b = [&](int i, int kt) {
+        if (MODE == NS_AXPY)
+            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_kn, (kt * BK + 8 * i) * p.ldb * 2, 0);
+        else
+            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_rp, kt * BK * 2 + i * 32 * p.ldb * 2, 0);
+    };
+    auto swrite_a = [&](int i, int st) {
+        *reinterpret_cast<i32x4*>(smem + w_rp + st * RP_B + i * 1024) = sa[i];
+    };
+    auto swrite_b = [&](int i, int st) {
+        if (MODE == NS_AXPY)
+            *reinterpret_cast<i32x4*>(smem + w_kn[i & 1] + st * KN_B + i * 8 * TILE * 2) = sb[i];
+        else
+            *reinterpret_cast<i32x4*>(smem + OFF_B + w_rp + st * RP_B + i * 1024) = sb[i];
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // fragment read bases
+    const int arow = lane & 31, khalf = lane >> 5;
+    const int rp_lane = arow * 32 + ((khalf ^ ((arow >> 3) & 1)) << 4);
+    const int r_a = wm0 * 32 + rp_lane;                               // + st*RP_B + kk*PLANE_B + i*1024
+    const int r_b = (diag ? 0 : OFF_B) + wn0 * 32 + rp_lane;          // + st*RP_B + kk*PLANE_B + j*1024
+    const int tg = lane >> 4, tix = lane & 15;
+    const int tr_k = 8 * (tg >> 1) + (tix >> 2);
+    const int tr_n = 16 * (tg & 1) + 4 * (tix & 3);
+    int r_tr[FN];                                                     // + st*KN_B + kk*8192 + h*2048
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int g = ((wn0 >> 5) + j) ^ (kn_swz(tr_k) % KN_NG);
+        r_tr[j] = OFF_B + tr_k * TILE * 2 + g * 64 + tr_n * 2;
+    }
+
+    constexpr int NRD = FM + ((MODE == NS_AXPY) ? 2 * FN : FN);
+    auto rd = [&](int r, int st, int kk, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN], bf16x4 (&tr)[FN][2]) {
+        if (r < FM) {
+            af[r] = *reinterpret_cast<const bf16x8*>(smem + r_a + st * RP_B + kk * PLANE_B + r * 1024);
+        } else if (MODE == NS_AXPY) {
+            const int j = (r - FM) >> 1, h = (r - FM) & 1;
+            tr[j][h] = lds_read_tr16(reinterpret_cast<const uint16_t*>(smem + r_tr[j] + st * KN_B + kk * 8192 + h * 2048));
+        } else {
+            const int j = r - FM;
+            bfr[j] = *reinterpret_cast<const bf16x8*>(smem + r_b + st * RP_B + kk * PLANE_B + j * 1024);
+        }
+    };
+    auto join_tr = [&](bf16x4 (&tr)[FN][2], bf16x8 (&bfr)[FN]) {
+        if (MODE == NS_AXPY) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                bfr[j] = __builtin_shufflevector(tr[j][0], tr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+
+    constexpr int NMF = FM * FN;                          // 16 MFMAs per sub-step
+    static_assert(NRD <= NMF, "read slots");
+    const int nk = p.K / BK;                              // a multiple of 4
+
+    bf16x8 fa[2][FM], fb[2][FN];
+    bf16x4 ftr[2][FN][2];
+    // The main loop is straight-line code: every condition below is a compile-time
+    // constant (diagonal tile or not, last two K steps or not), so the compiler's wait
+    // counts stay exact (a branch would make it wait for every outstanding load).
+    auto run = [&](auto diag_c) {
+        constexpr bool DG = decltype(diag_c)::value;
+        // prologue: K step 0 into stage 0, K step 1 into the staging registers
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) { gload_a(i, 0); if (!DG) gload_b(i, 0); }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) { swrite_a(i, 0); if (!DG) swrite_b(i, 0); }
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) { gload_a(i, 1); if (!DG) gload_b(i, 1); }
+        lds_wait_barrier();
+#pragma unroll
+        for (int r = 0; r < NRD; ++r) rd(r, 0, 0, fa[0], fb[0], ftr[0]);
+        join_tr(ftr[0], fb[0]);
+
+        // One K step from stage ST.  Sub-step 1 writes operand A of K step kt + 1 from the
+        // staging registers to the other stage and fetches its K step kt + 2; sub-step 2
+        // does the same for operand B; sub-step 3 opens with the barrier that publishes
+        // the other stage.  Each sub-step's first MFMA slots read the next sub-step's
+        // fragments.
+        auto kstep = [&](auto st_c, auto stage_c, auto load_c, int kt) {
+            constexpr int ST = decltype(st_c)::value, SN = ST ^ 1;
+            constexpr bool STAGE = decltype(stage_c)::value, LOAD = decltype(load_c)::value;
+#pragma unroll
+            for (int kk = 0; kk < KSUB; ++kk) {
+                const int cur = kk & 1, nxt = cur ^ 1;
+                const bool last = kk + 1 == KSUB;
+#pragma unroll
+                for (int f = 0; f < NMF; ++f) {
+                    const int i = f / FN, j = f % FN;
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (STAGE && last && f == 0) lds_wait_barrier();
+                    if (f < NRD && (!last || STAGE))
+                        rd(f, last ? SN : ST, last ? 0 : kk + 1, fa[nxt], fb[nxt], ftr[nxt]);
+                    if (STAGE && kk == 1 && f >= NMF - NCH) {
+                        swrite_a(f - (NMF - NCH), SN);
+                        if (LOAD) gload_a(f - (NMF - NCH), kt + 2);
+                    }
+                    if (STAGE && !DG && kk == 2 && f >= NMF - NCH) {
+                        swrite_b(f - (NMF - NCH), SN);
+                        if (LOAD) gload_b(f - (NMF - NCH), kt + 2);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (!last || STAGE) join_tr(ftr[nxt], fb[nxt]);
+            }
+        };
+        const std::true_type yes;
+        const std::false_type no;
+        for (int kt = 0; kt + 4 <= nk; kt += 2) {     // pairs whose K steps all fetch ahead
+            kstep(ic<0>{}, yes, yes, kt);
+            kstep(ic<1>{}, yes, yes, kt + 1);
+        }
+        kstep(ic<0>{}, yes, no, nk - 2);
+        kstep(ic<1>{}, no, no, nk - 1);
+    };
+    if (diag) run(std::true_type{});
+    else run(std::false_type{});
+    // ---- epilogue (as in ns_gemm_kernel) ---------------------------------------------------
+    uint16_t* out = p.out + (int64_t)mat * p.stride_o;
+    constexpr int EP_CHUNKS = TILE / 8;
+    constexpr int EP_ROWS_PER_INSTR = 512 / TILE;
+    constexpr int EP_INSTR = TILE / EP_ROWS_PER_INSTR;
+    constexpr int EP_PER_WAVE = EP_INSTR / NW;
+    uint16_t* Es = reinterpret_cast<uint16_t*>(smem);
+    if (MODE == NS_POLY || MODE == NS_AXPY) {
+        const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
+        lds_wait_barrier();                               // every wave is done with the K stages
+#pragma unroll 4
+        for (int i = 0; i < EP_PER_WAVE; ++i) {
+            const int q = wave + NW * i;
+            const int r = q * EP_ROWS_PER_INSTR + lane / EP_CHUNKS;
+            const int pc = lane % EP_CHUNKS;
+            const int g = (pc >> 2) ^ (ep_swz(r) % KN_NG);
+            load_to_lds(Eg + (int64_t)r * p.ldo + (g * 4 + (pc & 3)) * 8, Es + q * 512);
+        }
+        wait_vm<0, true>();
+        __syncthreads();
+    }
+    const int col_in = lane & 31, rsub = (lane >> 5) * 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int gc = tj * TILE + wn0 + j * 32 + col_in;
+            bf16x4 e[4];
+            if (MODE == NS_POLY || MODE == NS_AXPY) {
+                const int c = wn0 + j * 32 + tr_n;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r = wm0 + i * 32 + q * 8 + 4 * (tg >> 1) + (tix >> 2);
+                    const int g = (c >> 5) ^ (ep_swz(r) % KN_NG);
+                    e[q] = lds_read_tr16(Es + r * TILE + g * 32 + (c & 31));
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int gr0 = ti * TILE + wm0 + i * 32 + q * 8 + rsub;
+                uint16_t h[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    float val = acc[i][j][q * 4 + v];
+                    if (MODE == NS_POLY || MODE == NS_AXPY)
+                        val = p.alpha * (float)e[q][v] + p.gamma * val;
+                    h[v] = dev::f32_to_bf16(val);
+                    out[(int64_t)(gr0 + v) * p.ldo + gc] = h[v];
+                }
+                if (MODE != NS_AXPY && ti != tj) {
+                    uint2 m2;
+                    m2.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    m2.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                    *reinterpret_cast<uint2*>(out + (int64_t)gc * p.ldo + gr0) = m2;
+                }
+            }
+        }
+    }
+}
+
 template <int MODE, int TILE, int WM, int WN, int BK, int STAGES>
 hipError_t launch_cfg(const NsArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((ns_gemm_kernel<MODE, TILE, WM, WN, BK, STAGES>), dim3((unsigned)a.total_tiles),
@@ -438,7 +705,9 @@ hipError_t launch_cfg(const NsArgs& a, hipStream_t s) {
 template <int MODE>
 hipError_t launch_mode(int32_t tile, const NsArgs& a, hipStream_t s) {
     switch (tile) {
-        case TILE_256: return launch_cfg<MODE, 256, 2, 4, 64, 2>(a, s);
+        case TILE_256:
+            hipLaunchKernelGGL((ns_vs_kernel<MODE>), dim3((unsigned)a.total_tiles), dim3(256), 0, s, a);
+            return hipGetLastError();
         case TILE_128: return launch_cfg<MODE, 128, 2, 2, 64, 2>(a, s);
         case TILE_64: return launch_cfg<MODE, 64, 2, 2, 64, 2>(a, s);
         default: return hipErrorInvalidValue;

@@ -45,8 +45,12 @@ def _need_bytes(w):
 
 
 def _setup(key, sample_fn, reserve):
+    import gc
     from muon_newton_schulz_momentum_amd import harness, workloads as wl
     w = wl.get(key)
+    gc.collect()                      # earlier tests' tensors go back to the device
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     free, total = torch.cuda.mem_get_info()
     need = _need_bytes(w) + reserve
     print(f"[{key}] device memory: {free / 1e9:.1f} GB free of {total / 1e9:.1f} GB; need {need / 1e9:.1f} GB",
