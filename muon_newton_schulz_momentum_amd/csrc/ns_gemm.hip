@@ -13,11 +13,12 @@
 //   * NS_AXPY  X' = a X + B X: a full GEMM with the axpy fused into its epilogue.
 //
 // Two kernels share the tile order, the fragment layouts and the epilogue:
-//   * ns_vs_kernel (256 x 256 tiles, the large buckets): 4 waves of 128 x 128, one wave
-//     per SIMD with 256 accumulator registers each.  Operand tiles go global -> VGPR
-//     (buffer loads) -> LDS, one K step ahead of the LDS stage being multiplied; on
-//     gfx950 this path keeps more requests in flight than the direct-to-LDS loads when
-//     operands miss in L2 (measured 20-30 % more bytes per CU from the Infinity Cache).
+//   * ns_vs_kernel (256 x 256 tiles, the large buckets): 8 waves of 128 x 64, two waves
+//     per SIMD.  Operand tiles go global -> VGPR (buffer loads) -> LDS, one K step ahead
+//     of the LDS stage being multiplied; on gfx950 this path keeps more requests in
+//     flight than the direct-to-LDS loads when operands miss in L2 (measured 20-30 % more
+//     bytes per CU from the Infinity Cache).  The result tile is staged in LDS and leaves
+//     in 16-byte stores.
 //   * ns_gemm_kernel (128 and 64 tiles, the small buckets): operand tiles go from global
 //     memory straight into LDS with global_load_lds_dwordx4 (no VGPR staging): each
 //     lane's 16 bytes land at the instruction's LDS base + 16 * lane, and the lane picks
@@ -434,17 +435,27 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     }
 }
 
-// ---- 256 x 256 tiles, 4 waves of 128 x 128, operands staged through VGPRs --------------
+// ---- 256 x 256 tiles, operands staged through VGPRs -------------------------------------
 //
 // LDS layout (bytes).  Row panels (K contiguous in memory) are stored as 4 K-planes of 16
 // elements: row r, K chunk c (16 bytes, c = 0..7) lands at plane c/2, offset r*32 plus
-// 16 * ((c & 1) ^ ((r >> 3) & 1)); planes are 8192 + 64 bytes apart, so consecutive planes
-// start 64 bytes further round the 64 banks.  Every fragment read and every staging write
-// is then one per-lane base register plus a compile-time offset (plane, fragment, stage),
-// and the 16 lanes the LDS serves together touch 16 different 16-byte bank groups, for
-// reads (16 rows, one chunk) as well as for writes (2 rows, 8 chunks).  The K x N panel of
-// the axpy keeps the 512-byte rows with permuted 64-byte granules of ns_gemm_kernel.
+// 16 * ((c & 1) ^ ((r >> 3) & 1)); planes are 8192 + 32 bytes apart.  Every fragment read
+// and every staging write is then one per-lane base register plus a compile-time offset
+// (plane, fragment, stage).  Bank rules measured on gfx950 (SQ_LDS_BANK_CONFLICT): a
+// 128-bit read is served 16 lanes at a time across all 64 banks, a 128-bit write 8 lanes
+// at a time across 128 bytes of banks.  A fragment read (16 rows of one plane) covers 16
+// distinct 16-byte slots of the 256-byte bank line; a staging write (8 lanes: one row,
+// its 8 chunks in 4 planes) covers 8 distinct slots modulo 128 bytes thanks to the 32-byte
+// plane rotation.  The K x N panel of the axpy keeps the 512-byte rows with permuted
+// 64-byte granules of ns_gemm_kernel, whose writes (8 lanes: two 64-byte granules of
+// different parity) are conflict-free under the same rules.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// 8 waves (2 x 4) of 128 x 64: two waves per SIMD, 128 accumulators and 16 staging
+// registers each.  Measured on gfx950 against 4 waves of 128 x 128 (one wave per SIMD):
+// 4-12 % faster, since a wave waiting on LDS or a barrier leaves the matrix pipe to the
+// other wave of its SIMD.
+constexpr int VS_WM = 2, VS_WN = 4;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint16_t* base, int64_t elems) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(elems * 2), 0x00020000);
@@ -457,13 +468,18 @@ __device__ __forceinline__ void lds_wait_barrier() {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-template <int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void ns_vs_kernel(NsArgs p) {
-    constexpr int TILE = 256, BK = 64, NW = 4, WTM = 128, WTN = 128, FM = 4, FN = 4;
+template <int MODE, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
+void ns_vs_kernel(NsArgs p) {
+    constexpr int TILE = 256, BK = 64, NW = WM * WN, NT = 64 * NW;
+    constexpr int WTM = TILE / WM, WTN = TILE / WN, FM = WTM / 32, FN = WTN / 32;
+    constexpr int RP_ROWS = NT / 8;                   // row-panel rows per staging pass
+    constexpr int KN_ROWS = NT / 32;                  // K x N rows per staging pass
+    static_assert(RP_ROWS % 16 == 0, "staging rows keep the chunk swizzle");
     constexpr int KSUB = BK / 16;
-    constexpr int NCH = 8;                            // 16-byte chunks per thread and operand
+    constexpr int NCH = TILE * BK / 8 / NT;           // 16-byte chunks per thread and operand
     constexpr int KN_NG = TILE / 32;
-    constexpr int PLANE_B = 8192 + 64;
+    constexpr int PLANE_B = 8192 + 32;
     constexpr int RP_B = 4 * PLANE_B;                 // one row panel (256 x 64 bf16)
     constexpr int KN_B = 64 * TILE * 2;               // one K x N panel (64 x 256 bf16)
     constexpr int OFF_B = 2 * RP_B;                   // second operand's stages
@@ -474,7 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave >> 1) * WTM, wn0 = (wave & 1) * WTN;
+    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
 
     const int b = xcd_remap(blockIdx.x, gridDim.x);
     const int mat = b / p.tiles_per_mat;
@@ -490,7 +506,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int64_t b0 = (MODE == NS_AXPY) ? (int64_t)tj * TILE : (int64_t)tj * TILE * p.ldb;
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.opb + (int64_t)mat * p.stride_b + b0, p.stride_b - b0);
 
-    // staging: row panels -> rows row0 + 32 i, chunk ch; K x N -> rows klo + 8 i, chunk nc
+    // staging: row panels -> rows row0 + RP_ROWS i, chunk ch; K x N -> rows klo + KN_ROWS i,
+    // chunk nc.  The row swizzle bit (row >> 3) & 1 does not depend on i; the K x N granule
+    // swizzle depends at most on the parity of i.
     const int row0 = tid >> 3, ch = tid & 7;
     const int va = row0 * p.lda * 2 + ch * 16;
     const int vb_rp = row0 * p.ldb * 2 + ch * 16;
@@ -500,28 +518,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int w_kn[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-        const int swz = (klo & 3) | (4 * par);
+        const int swz = kn_swz(klo + KN_ROWS * par);
         w_kn[par] = OFF_B + klo * TILE * 2 + (((((nc >> 2) ^ (swz % KN_NG)) << 2) | (nc & 3)) << 4);
     }
 
     i32x4 sa[NCH], sb[NCH];
     auto gload_a = [&](int i, int kt) {
-        sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, kt * BK * 2 + i * 32 * p.lda * 2, 0);
+        sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, kt * BK * 2 + i * RP_ROWS * p.lda * 2, 0);
     };
     auto gload_b = [&](int i, int kt) {
         if (MODE == NS_AXPY)
-            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_kn, (kt * BK + 8 * i) * p.ldb * 2, 0);
+            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_kn, (kt * BK + KN_ROWS * i) * p.ldb * 2, 0);
         else
-            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_rp, kt * BK * 2 + i * 32 * p.ldb * 2, 0);
+            sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_rp, kt * BK * 2 + i * RP_ROWS * p.ldb * 2, 0);
     };
     auto swrite_a = [&](int i, int st) {
-        *reinterpret_cast<i32x4*>(smem + w_rp + st * RP_B + i * 1024) = sa[i];
+        *reinterpret_cast<i32x4*>(smem + w_rp + st * RP_B + i * RP_ROWS * 32) = sa[i];
     };
     auto swrite_b = [&](int i, int st) {
         if (MODE == NS_AXPY)
-            *reinterpret_cast<i32x4*>(smem + w_kn[i & 1] + st * KN_B + i * 8 * TILE * 2) = sb[i];
+            *reinterpret_cast<i32x4*>(smem + w_kn[i & 1] + st * KN_B + i * KN_ROWS * TILE * 2) = sb[i];
         else
-            *reinterpret_cast<i32x4*>(smem + OFF_B + w_rp + st * RP_B + i * 1024) = sb[i];
+            *reinterpret_cast<i32x4*>(smem + OFF_B + w_rp + st * RP_B + i * RP_ROWS * 32) = sb[i];
     };
 
     f32x16 acc[FM][FN];
@@ -567,8 +585,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     };
 
-    constexpr int NMF = FM * FN;                          // 16 MFMAs per sub-step
-    static_assert(NRD <= NMF, "read slots");
+    constexpr int NMF = FM * FN;                          // MFMAs per sub-step
+    static_assert(NRD <= NMF && NCH <= NMF, "issue slots");
     const int nk = p.K / BK;                              // a multiple of 4
 
     bf16x8 fa[2][FM], fb[2][FN];
@@ -606,7 +624,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int f = 0; f < NMF; ++f) {
                     const int i = f / FN, j = f % FN;
                     __builtin_amdgcn_sched_barrier(0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     if (STAGE && last && f == 0) lds_wait_barrier();
                     if (f < NRD && (!last || STAGE))
@@ -635,62 +653,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     if (diag) run(std::true_type{});
     else run(std::false_type{});
-    // ---- epilogue (as in ns_gemm_kernel) ---------------------------------------------------
+    // ---- epilogue ---------------------------------------------------------------------
+    // The MFMAs take the right operand first, so each 32 x 32 block is accumulated
+    // transposed: acc[i][j][4q + w] = D[wm0 + 32i + (lane & 31)][wn0 + 32j + 8q + 4(lane >> 5) + w],
+    // four consecutive columns of one output row per lane and q.  The result tile goes
+    // through LDS (row r at r * 512 bytes, 16-byte granule G stored at granule G ^ (r & 31))
+    // and leaves in 16-byte stores: whole 512-byte rows for the tile itself and, for the
+    // mirrored tile of the symmetric products, 64-byte row pieces assembled with
+    // transposing reads.  The E operand (A in NS_POLY, X in NS_AXPY) comes in through the
+    // same layout.
     uint16_t* out = p.out + (int64_t)mat * p.stride_o;
-    constexpr int EP_CHUNKS = TILE / 8;
-    constexpr int EP_ROWS_PER_INSTR = 512 / TILE;
-    constexpr int EP_INSTR = TILE / EP_ROWS_PER_INSTR;
-    constexpr int EP_PER_WAVE = EP_INSTR / NW;
-    uint16_t* Es = reinterpret_cast<uint16_t*>(smem);
+    char* T = smem;
+    auto tb = [](int r, int c) { return r * 512 + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2; };
+    const int er = lane & 31, ec = 4 * (lane >> 5);
+    lds_wait_barrier();                                   // every wave is done with the K stages
     if (MODE == NS_POLY || MODE == NS_AXPY) {
         const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
-        lds_wait_barrier();                               // every wave is done with the K stages
 #pragma unroll 4
-        for (int i = 0; i < EP_PER_WAVE; ++i) {
+        for (int i = 0; i < 128 / NW; ++i) {              // 1 KB (two rows) per instruction
             const int q = wave + NW * i;
-            const int r = q * EP_ROWS_PER_INSTR + lane / EP_CHUNKS;
-            const int pc = lane % EP_CHUNKS;
-            const int g = (pc >> 2) ^ (ep_swz(r) % KN_NG);
-            load_to_lds(Eg + (int64_t)r * p.ldo + (g * 4 + (pc & 3)) * 8, Es + q * 512);
+            const int r = 2 * q + (lane >> 5);
+            const int g = (lane & 31) ^ (r & 31);
+            load_to_lds(Eg + (int64_t)r * p.ldo + g * 8, reinterpret_cast<const uint16_t*>(T + q * 1024));
         }
         wait_vm<0, true>();
         __syncthreads();
     }
-    const int col_in = lane & 31, rsub = (lane >> 5) * 4;
+    uint2 res[FM][FN][4];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-            const int gc = tj * TILE + wn0 + j * 32 + col_in;
-            bf16x4 e[4];
-            if (MODE == NS_POLY || MODE == NS_AXPY) {
-                const int c = wn0 + j * 32 + tr_n;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r = wm0 + i * 32 + q * 8 + 4 * (tg >> 1) + (tix >> 2);
-                    const int g = (c >> 5) ^ (ep_swz(r) % KN_NG);
-                    e[q] = lds_read_tr16(Es + r * TILE + g * 32 + (c & 31));
-                }
-            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int gr0 = ti * TILE + wm0 + i * 32 + q * 8 + rsub;
-                uint16_t h[4];
+                float v[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    float val = acc[i][j][q * 4 + v];
-                    if (MODE == NS_POLY || MODE == NS_AXPY)
-                        val = p.alpha * (float)e[q][v] + p.gamma * val;
-                    h[v] = dev::f32_to_bf16(val);
-                    out[(int64_t)(gr0 + v) * p.ldo + gc] = h[v];
+                for (int w = 0; w < 4; ++w) v[w] = acc[i][j][4 * q + w];
+                if (MODE == NS_POLY || MODE == NS_AXPY) {
+                    const uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
+                    const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) v[w] = p.alpha * __builtin_bit_cast(float, ew[w]) + p.gamma * v[w];
                 }
-                if (MODE != NS_AXPY && ti != tj) {
-                    uint2 m2;
-                    m2.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-                    m2.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-                    *reinterpret_cast<uint2*>(out + (int64_t)gc * p.ldo + gr0) = m2;
-                }
+                res[i][j][q].x = (uint32_t)dev::f32_to_bf16(v[0]) | ((uint32_t)dev::f32_to_bf16(v[1]) << 16);
+                res[i][j][q].y = (uint32_t)dev::f32_to_bf16(v[2]) | ((uint32_t)dev::f32_to_bf16(v[3]) << 16);
             }
+        }
+    }
+    if (MODE == NS_POLY || MODE == NS_AXPY) lds_wait_barrier();   // E reads done before T is written
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec)) = res[i][j][q];
+    lds_wait_barrier();
+    // the tile: 256 rows x 32 granules, whole rows per 32 lanes
+    uint16_t* orow = out + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
+#pragma unroll 4
+    for (int s2 = 0; s2 < TILE * 32 / NT; ++s2) {
+        const int gi = tid + NT * s2;
+        const int r = gi >> 5, g = gi & 31;
+        const uint4 v = *reinterpret_cast<const uint4*>(T + r * 512 + ((g ^ (r & 31)) << 4));
+        *reinterpret_cast<uint4*>(orow + (int64_t)r * p.ldo + g * 8) = v;
+    }
+    // the mirrored tile (symmetric products, off the diagonal): row c of it is column c of
+    // the tile.  A transposing read over 16 lanes turns 4 tile rows x 16 columns into 16
+    // mirrored rows x 4 elements; two of them give each lane 16 bytes of one mirrored row.
+    if (MODE != NS_AXPY && ti != tj) {
+        uint16_t* omir = out + (int64_t)tj * TILE * p.ldo + (int64_t)ti * TILE;
+        const int x = lane & 15, grp = lane >> 4;
+        const int ax = x & 3, mx = x >> 2;
+#pragma unroll 2
+        for (int u = wave; u < 128; u += NW) {            // 16 columns x 32 rows per unit
+            const int c0 = (u & 15) * 16, r0 = (u >> 4) * 32 + 8 * grp;
+            const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(T + tb(r0 + mx, c0 + 4 * ax)));
+            const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(T + tb(r0 + 4 + mx, c0 + 4 * ax)));
+            const bf16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            *reinterpret_cast<bf16x8*>(omir + (int64_t)(c0 + x) * p.ldo + r0) = v8;
         }
     }
 }
@@ -706,7 +747,8 @@ template <int MODE>
 hipError_t launch_mode(int32_t tile, const NsArgs& a, hipStream_t s) {
     switch (tile) {
         case TILE_256:
-            hipLaunchKernelGGL((ns_vs_kernel<MODE>), dim3((unsigned)a.total_tiles), dim3(256), 0, s, a);
+            hipLaunchKernelGGL((ns_vs_kernel<MODE, VS_WM, VS_WN>), dim3((unsigned)a.total_tiles),
+                               dim3(64 * VS_WM * VS_WN), 0, s, a);
             return hipGetLastError();
         case TILE_128: return launch_cfg<MODE, 128, 2, 2, 64, 2>(a, s);
         case TILE_64: return launch_cfg<MODE, 64, 2, 2, 64, 2>(a, s);
