@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "ladder24"
 METRIC = "batched Newton–Schulz TFLOP/s (% bf16 MFMA peak) + Muon step ms per shape mix"
-KERNEL_SOURCES = ["ns_gemm.hip", "elementwise.hip", "api.hip", "kernels.h", "device_common.h"]
+KERNEL_SOURCES = ["ns_gemm.hip", "ns_small.hip", "elementwise.hip", "api.hip", "kernels.h", "device_common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -172,7 +172,7 @@ def main(argv=None):
         if n == 0:
             continue
         name = L.muon_kernel_name(k).decode()
-        mfma = k in (L.MUON_KERNEL_SYRK, L.MUON_KERNEL_SYRK_POLY, L.MUON_KERNEL_GEMM_AXPY)
+        mfma = k in (L.MUON_KERNEL_SYRK, L.MUON_KERNEL_SYRK_POLY, L.MUON_KERNEL_GEMM_AXPY, L.MUON_KERNEL_NS_SMALL)
         rate = work / (ms * 1e-3) / (1e12 if mfma else 1e9)
         peak = PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS
         kernels[name] = {
@@ -193,7 +193,8 @@ def main(argv=None):
     }
 
     conv, alg = w.ns_flops()
-    ns_ms = sum(kernels[k]["ms_per_step"] for k in ("syrk", "syrk_poly", "gemm_axpy", "normalize", "norm_finalize")
+    ns_ms = sum(kernels[k]["ms_per_step"] for k in ("syrk", "syrk_poly", "gemm_axpy", "normalize", "norm_finalize",
+                                                    "ns_small")
                 if k in kernels)
     value = conv / (ms_per_step * 1e-3) / 1e12
 

@@ -89,7 +89,13 @@ typedef struct muon_plan_opts {
      * descriptors; entries of excluded parameters are ignored).  NULL means s_i = 1.
      * The pages give no scale rule; the scale is a free per-matrix factor. */
     const float* scale;
+    /* MUON_PLAN_* bits; 0 for the defaults. */
+    uint32_t flags;
 } muon_plan_opts;
+
+/* Orthogonalise small matrices with the tiled kernels too, instead of the fused
+ * whole-iteration kernel (both give bitwise the same result; this exists to show it). */
+#define MUON_PLAN_TILED_SMALL 1u
 
 typedef struct muon_plan muon_plan;
 
@@ -102,6 +108,8 @@ typedef struct muon_chunk_info {
     int32_t tile;          /* Newton–Schulz output tile edge                           */
     int32_t grad_dtype;
     int32_t shared_region; /* 1 when this chunk shares its workspace region            */
+    int32_t fused_small;   /* 1 when one fused kernel runs this chunk's whole NS        */
+    int32_t reserved;
     double flops_conventional; /* per NS iteration: 4 m^2 n + 2 m^3, times count        */
     double flops_algorithmic;  /* per NS iteration: m(m+1)n + m^2(m+1) + 2 m^2 n, x count */
     double bytes_momentum;     /* algorithmic HBM bytes of the momentum kernel          */
@@ -227,7 +235,8 @@ MUON_API void muon_graph_destroy(muon_graph* graph);
 #define MUON_KERNEL_SYRK_POLY 4
 #define MUON_KERNEL_GEMM_AXPY 5
 #define MUON_KERNEL_APPLY 6
-#define MUON_KERNEL_COUNT 7
+#define MUON_KERNEL_NS_SMALL 7
+#define MUON_KERNEL_COUNT 8
 
 /* Start recording a HIP event pair around every kernel launch of this plan (up to
  * `capacity` launches; later ones go unrecorded).  capacity = 0 stops recording.

@@ -43,7 +43,10 @@ MUON_KERNEL_SYRK = 3
 MUON_KERNEL_SYRK_POLY = 4
 MUON_KERNEL_GEMM_AXPY = 5
 MUON_KERNEL_APPLY = 6
-MUON_KERNEL_COUNT = 7
+MUON_KERNEL_NS_SMALL = 7
+MUON_KERNEL_COUNT = 8
+
+MUON_PLAN_TILED_SMALL = 1
 
 
 class muon_param_desc(C.Structure):
@@ -53,13 +56,14 @@ class muon_param_desc(C.Structure):
 
 
 class muon_plan_opts(C.Structure):
-    _fields_ = [("max_workspace_bytes", C.c_uint64), ("scale", C.POINTER(C.c_float))]
+    _fields_ = [("max_workspace_bytes", C.c_uint64), ("scale", C.POINTER(C.c_float)), ("flags", C.c_uint32)]
 
 
 class muon_chunk_info(C.Structure):
     _fields_ = [("m", C.c_int64), ("n", C.c_int64), ("m_pad", C.c_int64), ("n_pad", C.c_int64),
                 ("count", C.c_int64), ("bucket", C.c_int32), ("tile", C.c_int32),
                 ("grad_dtype", C.c_int32), ("shared_region", C.c_int32),
+                ("fused_small", C.c_int32), ("reserved", C.c_int32),
                 ("flops_conventional", C.c_double), ("flops_algorithmic", C.c_double),
                 ("bytes_momentum", C.c_double), ("bytes_apply", C.c_double),
                 ("region_offset", C.c_uint64), ("region_bytes", C.c_uint64)]

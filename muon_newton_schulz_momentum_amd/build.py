@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuon.so")
 
-HIP_SOURCES = ["api.hip", "elementwise.hip", "ns_gemm.hip"]
+HIP_SOURCES = ["api.hip", "elementwise.hip", "ns_gemm.hip", "ns_small.hip"]
 CXX_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 #include "plan_internal.h"
@@ -153,6 +154,72 @@ muon_status ns_chunk(const muon_plan* p, const Chunk& c, float a_, float b_, flo
     return MUON_OK;
 }
 
+// Algorithmic FLOPs of one Newton–Schulz iteration over a chunk (the three products,
+// the symmetric ones on one triangle).
+double ns_iter_flops(const Chunk& c) {
+    const double m = (double)c.m, n = (double)c.n;
+    return (double)c.count * (m * (m + 1.0) * n + m * m * (m + 1.0) + 2.0 * m * m * n);
+}
+
+// The fused small-matrix kernel over the given chunks (all with Chunk::fused), in
+// launches of up to SMALL_NS_MAX_JOBS chunks: normaliser, normalisation and every
+// iteration in one launch.
+muon_status ns_small_chunks(const muon_plan* p, const std::vector<int32_t>& idx, float a_, float b_, float c_,
+                            int32_t steps, float eps, hipStream_t s) {
+    for (size_t g0 = 0; g0 < idx.size(); g0 += SMALL_NS_MAX_JOBS) {
+        SmallNsArgs A{};
+        int64_t total = 0;
+        double work = 0.0;
+        for (size_t k = g0; k < idx.size() && k < g0 + SMALL_NS_MAX_JOBS; ++k) {
+            const Chunk& ch = p->chunks[(size_t)idx[k]];
+            SmallJob& J = A.job[A.n_jobs++];
+            J.xq = at<const uint16_t>(p, ch.off_xq);
+            J.xp = at<uint16_t>(p, ch.off_xp);
+            J.partials = at<const double>(p, ch.off_part);
+            J.ew_tiles = ch.ew_tiles;
+            J.m = (int32_t)ch.m;
+            J.n = (int32_t)ch.n;
+            J.np = (int32_t)ch.np;
+            J.first = (int32_t)total;
+            total += ch.count;
+            work += steps * ns_iter_flops(ch);
+        }
+        A.steps = steps;
+        A.a = a_;
+        A.b = b_;
+        A.c = c_;
+        A.eps = (double)eps;
+        TimedLaunch tl(p, MUON_KERNEL_NS_SMALL, work, s);
+        const hipError_t e = launch_ns_small(A, total, s);
+        tl.done(s);
+        if (e != hipSuccess) return hip_fail(e, "fused small-matrix NS kernel launch");
+    }
+    return MUON_OK;
+}
+
+// Newton–Schulz for one chunk, by whichever path the plan chose for it.
+muon_status ns_one(const muon_plan* p, int32_t i, float a_, float b_, float c_, int32_t steps, float eps,
+                   hipStream_t s) {
+    const Chunk& ch = p->chunks[(size_t)i];
+    if (ch.fused) return ns_small_chunks(p, std::vector<int32_t>{i}, a_, b_, c_, steps, eps, s);
+    return ns_chunk(p, ch, a_, b_, c_, steps, eps, s);
+}
+
+// Newton–Schulz for every chunk (their regions are distinct): all fused chunks in grouped
+// launches, then the tiled ones.
+muon_status ns_all(const muon_plan* p, float a_, float b_, float c_, int32_t steps, float eps, hipStream_t s) {
+    std::vector<int32_t> small;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
+        if (p->chunks[(size_t)i].fused) small.push_back(i);
+    muon_status st = ns_small_chunks(p, small, a_, b_, c_, steps, eps, s);
+    if (st != MUON_OK) return st;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        const Chunk& ch = p->chunks[(size_t)i];
+        if (!ch.fused && (st = ns_chunk(p, ch, a_, b_, c_, steps, eps, s)) != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
 muon_status apply_chunk(const muon_plan* p, const Chunk& c, float lr, float wd, hipStream_t s) {
     ApplyArgs a;
     a.tbl = at<const MatEntry>(p, c.off_table);
@@ -172,15 +239,26 @@ muon_status apply_chunk(const muon_plan* p, const Chunk& c, float lr, float wd, 
 
 bool finite(float v) { return std::isfinite(v); }
 
-// Steps 1, 3 and 5 for one chunk (-1 = every chunk, in order) on one stream.
+// Steps 1, 3 and 5 for one chunk, or for every chunk (-1) on one stream.  With distinct
+// regions every chunk's momentum runs first, then Newton–Schulz (small chunks grouped),
+// then every apply; chunks that share a region go through all three in turn.
 muon_status step_chunks(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,
                         float eps, float lr, float wd, hipStream_t s) {
     muon_status st;
-    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+    const int32_t nc = (int32_t)p->chunks.size();
+    if (chunk == -1 && !p->shared_regions) {
+        for (int32_t i = 0; i < nc; ++i)
+            if ((st = momentum_chunk(p, p->chunks[(size_t)i], beta, s)) != MUON_OK) return st;
+        if ((st = ns_all(p, a, b, c, steps, eps, s)) != MUON_OK) return st;
+        for (int32_t i = 0; i < nc; ++i)
+            if ((st = apply_chunk(p, p->chunks[(size_t)i], lr, wd, s)) != MUON_OK) return st;
+        return MUON_OK;
+    }
+    for (int32_t i = 0; i < nc; ++i) {
         if (chunk != -1 && i != chunk) continue;
         const Chunk& ch = p->chunks[(size_t)i];
         if ((st = momentum_chunk(p, ch, beta, s)) != MUON_OK) return st;
-        if ((st = ns_chunk(p, ch, a, b, c, steps, eps, s)) != MUON_OK) return st;
+        if ((st = ns_one(p, i, a, b, c, steps, eps, s)) != MUON_OK) return st;
         if ((st = apply_chunk(p, ch, lr, wd, s)) != MUON_OK) return st;
     }
     return MUON_OK;
@@ -262,11 +340,8 @@ muon_status muon_ns_batched(const muon_plan* p, int32_t chunk, float a, float b,
     if (!finite(a) || !finite(b) || !finite(c) || !finite(eps) || eps < 0.f)
         return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched: coefficients must be finite and eps >= 0");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
-        if (chunk != -1 && i != chunk) continue;
-        if ((st = ns_chunk(p, p->chunks[(size_t)i], a, b, c, steps, eps, s)) != MUON_OK) return st;
-    }
-    return MUON_OK;
+    if (chunk == -1) return ns_all(p, a, b, c, steps, eps, s);
+    return ns_one(p, chunk, a, b, c, steps, eps, s);
 }
 
 muon_status muon_apply(const muon_plan* p, int32_t chunk, float lr, float wd, void* stream) {
@@ -430,6 +505,7 @@ const char* muon_kernel_name(int32_t k) {
         case MUON_KERNEL_SYRK_POLY: return "syrk_poly";
         case MUON_KERNEL_GEMM_AXPY: return "gemm_axpy";
         case MUON_KERNEL_APPLY: return "apply";
+        case MUON_KERNEL_NS_SMALL: return "ns_small";
         default: return "unknown";
     }
 }

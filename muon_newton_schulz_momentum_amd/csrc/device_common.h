@@ -43,6 +43,14 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double x) {
     return (uint16_t)(__float_as_uint((float)r) >> 16);
 }
 
+// The epilogue combine of the Newton–Schulz products, alpha * E + gamma * P, as one
+// pinned sequence: gamma * P rounded to float32, then one fused multiply-add.  Written out
+// so that every kernel (tiled or fused) rounds it the same way, whatever the compiler
+// would contract on its own.
+__device__ __forceinline__ float ns_combine(float alpha, float e, float gamma, float prod) {
+    return __builtin_fmaf(alpha, e, gamma * prod);
+}
+
 // Sum over the 64 lanes of a wavefront by butterfly.  The order of additions is fixed,
 // so the result is the same on every run (no atomics anywhere in the reductions).
 __device__ __forceinline__ double wave_sum(double v) {

@@ -66,10 +66,34 @@ struct NsArgs {
     float gamma;           // POLY: c (times the product); AXPY: 1
 };
 
+// Whole Newton–Schulz of small matrices (canonical m <= 64, padded n <= SMALL_NS_MAX_N,
+// see plan_internal.h),
+// one workgroup per matrix; every job is one chunk of such matrices.
+
+constexpr int SMALL_NS_MAX_JOBS = 8;
+
+struct SmallJob {
+    const uint16_t* xq;        // X0: count matrices of 64 x np bf16
+    uint16_t* xp;              // O: count matrices of 64 x np bf16
+    const double* partials;    // count * ew_tiles sums of squares
+    int64_t ew_tiles;
+    int32_t m, n, np;
+    int32_t first;             // first workgroup of this job
+};
+
+struct SmallNsArgs {
+    SmallJob job[SMALL_NS_MAX_JOBS];
+    int32_t n_jobs;
+    int32_t steps;
+    float a, b, c;
+    double eps;
+};
+
 hipError_t launch_momentum(const MomentumArgs& a, int32_t grad_dtype, hipStream_t s);
 hipError_t launch_finalize(const FinalizeArgs& a, int64_t count, hipStream_t s);
 hipError_t launch_normalize(const NormalizeArgs& a, hipStream_t s);
 hipError_t launch_apply(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s);
+hipError_t launch_ns_small(const SmallNsArgs& a, int64_t total, hipStream_t s);
 
 }  // namespace muon

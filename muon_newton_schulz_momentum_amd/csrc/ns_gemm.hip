@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
                 for (int v = 0; v < 4; ++v) {
                     float val = acc[i][j][q * 4 + v];
                     if (MODE == NS_POLY || MODE == NS_AXPY)
-                        val = p.alpha * (float)e[q][v] + p.gamma * val;
+                        val = dev::ns_combine(p.alpha, (float)e[q][v], p.gamma, val);
                     h[v] = dev::f32_to_bf16(val);
                     out[(int64_t)(gr0 + v) * p.ldo + gc] = h[v];
                 }
@@ -693,7 +693,7 @@ void ns_vs_kernel(NsArgs p) {
                     const uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
                     const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) v[w] = p.alpha * __builtin_bit_cast(float, ew[w]) + p.gamma * v[w];
+                    for (int w = 0; w < 4; ++w) v[w] = dev::ns_combine(p.alpha, __builtin_bit_cast(float, ew[w]), p.gamma, v[w]);
                 }
                 res[i][j][q].x = (uint32_t)dev::f32_to_bf16(v[0]) | ((uint32_t)dev::f32_to_bf16(v[1]) << 16);
                 res[i][j][q].y = (uint32_t)dev::f32_to_bf16(v[2]) | ((uint32_t)dev::f32_to_bf16(v[3]) << 16);

@@ -100,6 +100,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (n > 0 && !params) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: params is NULL");
     const uint64_t cap = opts ? opts->max_workspace_bytes : 0;
     const float* scales = opts ? opts->scale : nullptr;
+    const uint32_t flags = opts ? opts->flags : 0u;
 
     // ---- validate every descriptor -----------------------------------------------------
     std::vector<Interval> ivs;
@@ -191,6 +192,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     for (const BucketGeo& g : geo)
         total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 6 * WS_ALIGN;
     p->shared_regions = cap != 0 && total > cap;
+    p->flags = flags;
 
     int32_t bucket_id = 0;
     for (const BucketGeo& g : geo) {
@@ -217,6 +219,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
             Chunk ch{};
             ch.bucket = bucket_id; ch.grad_dtype = g.gdt;
             ch.m = g.m; ch.n = g.n; ch.mp = g.mp; ch.np = g.np; ch.tile = g.tile;
+            ch.fused = !(flags & MUON_PLAN_TILED_SMALL) && g.mp == 64 && g.np <= SMALL_NS_MAX_N;
             ch.count = cnt; ch.first = (int64_t)p->table.size(); ch.ew_tiles = g.ew;
             ch.off_table = (uint64_t)ch.first * sizeof(MatEntry);
             const int32_t cidx = (int32_t)p->chunks.size();
@@ -277,6 +280,8 @@ muon_status muon_plan_info(const muon_plan* plan, int32_t chunk, muon_chunk_info
     out->m = c.m; out->n = c.n; out->m_pad = c.mp; out->n_pad = c.np; out->count = c.count;
     out->bucket = c.bucket; out->tile = c.tile; out->grad_dtype = c.grad_dtype;
     out->shared_region = plan->shared_regions ? 1 : 0;
+    out->fused_small = c.fused ? 1 : 0;
+    out->reserved = 0;
     const double m = (double)c.m, n = (double)c.n, k = (double)c.count;
     out->flops_conventional = k * (4.0 * m * m * n + 2.0 * m * m * m);
     out->flops_algorithmic = k * (m * (m + 1.0) * n + m * m * (m + 1.0) + 2.0 * m * m * n);

@@ -32,8 +32,9 @@ struct Chunk {
     int32_t bucket;
     int32_t grad_dtype;
     int64_t m, n;            // canonical shape
-    int64_t mp, np;          // padded shape: mp multiple of tile, np multiple of 256
+    int64_t mp, np;          // padded shape: multiples of the tile
     int32_t tile;
+    bool fused = false;      // the whole NS runs in the fused small-matrix kernel
     int64_t count;           // matrices in this chunk
     int64_t first;           // first row of this chunk in the matrix table
     // elementwise tiling: 64 x 64 tiles over rows x cols (same count for both orientations)
@@ -74,6 +75,7 @@ struct muon_plan {
     int32_t n_buckets = 0;
     int64_t n_included = 0, n_excluded = 0;
     bool shared_regions = false;
+    uint32_t flags = 0;      // MUON_PLAN_* bits
     uint64_t table_bytes = 0;
     uint64_t ws_bytes = 0;
     // bind state
@@ -99,6 +101,7 @@ muon_status set_error(muon_status s, const std::string& msg);
 void clear_error();
 
 constexpr int EW_TILE = 64;          // elementwise tile edge
+constexpr int SMALL_NS_MAX_N = 1024; // widest padded n of the fused small-matrix kernel
 constexpr uint64_t WS_ALIGN = 256;   // workspace sub-buffer alignment
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }

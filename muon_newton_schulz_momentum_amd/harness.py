@@ -58,7 +58,7 @@ class Plan:
     """One bound libmuon plan over a list of parameters."""
 
     def __init__(self, params: Sequence[ParamTensors], max_workspace_bytes: int = 0,
-                 scales: Optional[Sequence[float]] = None, device=None, bind: bool = True):
+                 scales: Optional[Sequence[float]] = None, device=None, bind: bool = True, flags: int = 0):
         self.params = list(params)
         n = len(self.params)
         self._descs = (L.muon_param_desc * max(n, 1))()
@@ -66,6 +66,7 @@ class Plan:
             self._descs[i] = _desc(p)
         opts = L.muon_plan_opts()
         opts.max_workspace_bytes = int(max_workspace_bytes)
+        opts.flags = int(flags)
         self._scales = None
         if scales is not None:
             self._scales = (C.c_float * max(n, 1))(*[float(s) for s in scales])

@@ -53,9 +53,10 @@ def _descs(shapes, gdtype=L.MUON_DTYPE_F32, mem=None):
     return arr
 
 
-def _plan(arr, n=None, cap=0, scales=None):
+def _plan(arr, n=None, cap=0, scales=None, flags=0):
     opts = L.muon_plan_opts()
     opts.max_workspace_bytes = cap
+    opts.flags = flags
     keep = None
     if scales is not None:
         keep = (C.c_float * len(scales))(*scales)
@@ -270,3 +271,17 @@ def test_step_calls_refused_before_bind_and_bind_checks():
     assert L.muon_status_string(L.MUON_ERR_STALE_PLAN) == b"stale plan"
     L.muon_plan_destroy(p)
     L.muon_plan_destroy(None)
+
+
+def test_fused_small_path_is_chosen_by_shape_and_flag():
+    # canonical m <= 64 (padded to one 64-row tile) and padded n <= 1024 take the fused
+    # whole-iteration kernel; everything else the tiled kernels
+    shapes = [(64, 128), (300, 17), (32, 1000), (64, 1088), (65, 128), (1, 4096), (1, 64)]
+    want = {(64, 128): 1, (17, 300): 1, (32, 1000): 1, (64, 1088): 0, (65, 128): 0, (1, 4096): 0, (1, 64): 1}
+    for flags, expect in ((0, want), (L.MUON_PLAN_TILED_SMALL, {k: 0 for k in want})):
+        st, p = _plan(_descs(shapes), flags=flags)
+        assert st == 0
+        got = {(i["m"], i["n"]): i["fused_small"] for i in _infos(p)}
+        assert got == expect
+        L.muon_plan_destroy(p)
+    assert L.muon_kernel_name(L.MUON_KERNEL_NS_SMALL) == b"ns_small"

@@ -54,7 +54,12 @@ def _replay_against_eager(shapes, seed, replays, max_ws=0):
     plan = harness.Plan(graph_p, max_workspace_bytes=max_ws)
     torch.cuda.synchronize()
     g = plan.capture(BETA, LR, WD, A, B, C, K, EPS)
-    assert g.nodes == plan.n_chunks * (4 + 3 * K)
+    fused = sum(plan.chunk_info(c).fused_small for c in range(plan.n_chunks))
+    tiled = plan.n_chunks - fused
+    # momentum + apply per chunk; tiled chunks: finalize, normalize, 3 per iteration;
+    # fused chunks: one grouped launch (up to 8 chunks) when the chunks have their own regions
+    small_launches = fused if plan.chunk_info(0).shared_region else -(-fused // 8)
+    assert g.nodes == 2 * plan.n_chunks + tiled * (2 + 3 * K) + small_launches
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed + 1)
     for r in range(replays):
