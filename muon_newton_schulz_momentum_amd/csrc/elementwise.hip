@@ -71,9 +71,92 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
         uint16_t* X = a.xq + mat * a.mat_stride;
         const int64_t c = c0 + cg * 4;
         double ss = 0.0;
+        // A parameter stored as it is (not transposed) is streamed flat: tile t covers its
+        // elements [4096 t, 4096 t + 4096) in row-major order, lane l of a wave handles 16
+        // bytes at 1 KB steps, so every wave access is 1 KB contiguous (a 64 x 64 tile
+        // would touch 64 separate 256-byte row pieces).  All loads go out before the first
+        // store.  The tile's sum of squares lands in its own partial, as in the 2-D path.
+        const bool flat = !e.trans && vec && (a.np & 3) == 0;
+        if (flat) {
+            const int64_t nel = e.rows * e.cols;
+            const int64_t e0 = tile * (T * T) + tid * 4;
+            float4 mv[4];
+            float gv[4][4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t idx = e0 + k * 1024;
+                if (idx < nel) {
+                    mv[k] = *reinterpret_cast<const float4*>(e.m + idx);
+                    load_grad4<GDT>(e.g, idx, gv[k]);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t idx = e0 + k * 1024;
+                if (idx >= nel) continue;
+                float4 mn;
+                mn.x = momentum_elem(mv[k].x, gv[k][0], beta, omb);
+                mn.y = momentum_elem(mv[k].y, gv[k][1], beta, omb);
+                mn.z = momentum_elem(mv[k].z, gv[k][2], beta, omb);
+                mn.w = momentum_elem(mv[k].w, gv[k][3], beta, omb);
+                *reinterpret_cast<float4*>(e.m + idx) = mn;
+                const uint16_t xb[4] = {f32_to_bf16(mn.x), f32_to_bf16(mn.y), f32_to_bf16(mn.z), f32_to_bf16(mn.w)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const double x = (double)bf16_to_f32(xb[j]);
+                    ss += x * x;
+                }
+                // the 4 elements share a row (cols is a multiple of 4)
+                const int64_t xi = (a.np == e.cols) ? idx : (idx / e.cols) * a.np + idx % e.cols;
+                uint2 v;
+                v.x = (uint32_t)xb[0] | ((uint32_t)xb[1] << 16);
+                v.y = (uint32_t)xb[2] | ((uint32_t)xb[3] << 16);
+                *reinterpret_cast<uint2*>(X + xi) = v;
+            }
+        }
+        // Interior tile: every load of the tile is issued before the first store, so each
+        // lane keeps 8 loads in flight (stores to M may alias later loads of M as far as
+        // the compiler knows, so the general loop below cannot be reordered that way).
+        const bool full = !flat && vec && r0 + T <= e.rows && c0 + T <= e.cols && (a.np & 3) == 0;
+        if (full) {
+            float4 mv[4];
+            float gv[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t base = (r0 + rg + 16 * i) * e.cols + c;
+                mv[i] = *reinterpret_cast<const float4*>(e.m + base);
+                load_grad4<GDT>(e.g, base, gv[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = r0 + rg + 16 * i;
+                const int64_t base = r * e.cols + c;
+                float4 mn;
+                mn.x = momentum_elem(mv[i].x, gv[i][0], beta, omb);
+                mn.y = momentum_elem(mv[i].y, gv[i][1], beta, omb);
+                mn.z = momentum_elem(mv[i].z, gv[i][2], beta, omb);
+                mn.w = momentum_elem(mv[i].w, gv[i][3], beta, omb);
+                *reinterpret_cast<float4*>(e.m + base) = mn;
+                const uint16_t xb[4] = {f32_to_bf16(mn.x), f32_to_bf16(mn.y), f32_to_bf16(mn.z), f32_to_bf16(mn.w)};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const double x = (double)bf16_to_f32(xb[j]);
+                    ss += x * x;
+                }
+                if (!e.trans) {
+                    uint2 v;
+                    v.x = (uint32_t)xb[0] | ((uint32_t)xb[1] << 16);
+                    v.y = (uint32_t)xb[2] | ((uint32_t)xb[3] << 16);
+                    *reinterpret_cast<uint2*>(X + r * a.np + c) = v;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) tr[cg * 4 + j][rg + 16 * i] = xb[j];
+                }
+            }
+        }
 
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4 && !full && !flat; ++i) {
             const int64_t r = r0 + rg + 16 * i;
             uint16_t xb[4] = {0, 0, 0, 0};
             int nvalid = 0;
@@ -167,33 +250,52 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
     }
 }
 
+__device__ __forceinline__ uint4 normalize_unit(uint4 in, int64_t c, int64_t n, double s) {
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (c + j < n) {
+            const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
+            const uint32_t y = f64_to_bf16((double)bf16_to_f32(h) * s);
+            o[j >> 1] |= (j & 1) ? (y << 16) : y;
+        }
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Each thread takes UPT units of 8 elements, one block-width apart, and issues all its
+// loads before the first store.
+constexpr int UPT = 4;
+
 __global__ __launch_bounds__(256) void normalize_kernel(NormalizeArgs a) {
     const int64_t upr = a.np >> 3;             // 8-element units per row
     const int64_t per_mat = a.mp * upr;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < a.total_units; u += stride) {
-        const int64_t mat = u / per_mat;
-        const int64_t rem = u - mat * per_mat;
-        const int64_t r = rem / upr;
-        const int64_t c = (rem - r * upr) * 8;
-        const int64_t off = mat * a.mp * a.np + r * a.np + c;
-        uint4 out = make_uint4(0, 0, 0, 0);
-        if (r < a.m && c < a.n) {
-            const double s = a.inv[mat];
-            const uint4 in = *reinterpret_cast<const uint4*>(a.src + off);
-            const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-            uint32_t o[4] = {0, 0, 0, 0};
+    const int64_t span = (int64_t)gridDim.x * blockDim.x * UPT;
+    for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * UPT + threadIdx.x; u0 < a.total_units; u0 += span) {
+        uint4 in[UPT];
+        int64_t off[UPT], cc[UPT], mm[UPT];
+        bool live[UPT];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (c + j < a.n) {
-                    const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
-                    const uint32_t y = f64_to_bf16((double)bf16_to_f32(h) * s);
-                    o[j >> 1] |= (j & 1) ? (y << 16) : y;
-                }
-            }
-            out = make_uint4(o[0], o[1], o[2], o[3]);
+        for (int k = 0; k < UPT; ++k) {
+            const int64_t u = u0 + (int64_t)k * blockDim.x;
+            const int64_t mat = u / per_mat;
+            const int64_t rem = u - mat * per_mat;
+            const int64_t r = rem / upr;
+            const int64_t c = (rem - r * upr) * 8;
+            off[k] = mat * a.mp * a.np + r * a.np + c;
+            cc[k] = c;
+            mm[k] = mat;
+            live[k] = u < a.total_units && r < a.m && c < a.n;
+            in[k] = live[k] ? *reinterpret_cast<const uint4*>(a.src + off[k]) : make_uint4(0, 0, 0, 0);
         }
-        *reinterpret_cast<uint4*>(a.dst + off) = out;
+#pragma unroll
+        for (int k = 0; k < UPT; ++k) {
+            const int64_t u = u0 + (int64_t)k * blockDim.x;
+            if (u >= a.total_units) continue;
+            const uint4 out = live[k] ? normalize_unit(in[k], cc[k], a.n, a.inv[mm[k]]) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(a.dst + off[k]) = out;
+        }
     }
 }
 
@@ -241,8 +343,68 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a) {
             __syncthreads();
         }
 
+        // Flat streaming for parameters stored as they are (see the momentum kernel).
+        const bool flat = !e.trans && vec && (a.np & 3) == 0;
+        if (flat) {
+            const int64_t nel = e.rows * e.cols;
+            const int64_t e0 = tile * (T * T) + tid * 4;
+            float4 wv[4];
+            uint2 ov[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int k = 0; k < 4; ++k) {
+                const int64_t idx = e0 + k * 1024;
+                if (idx < nel) {
+                    wv[k] = *reinterpret_cast<const float4*>(e.w + idx);
+                    const int64_t xi = (a.np == e.cols) ? idx : (idx / e.cols) * a.np + idx % e.cols;
+                    ov[k] = *reinterpret_cast<const uint2*>(O + xi);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t idx = e0 + k * 1024;
+                if (idx >= nel) continue;
+                float4 w = wv[k];
+                w.x = apply_elem(w.x, bf16_to_f32(ov[k].x & 0xffffu), a.d, u);
+                w.y = apply_elem(w.y, bf16_to_f32(ov[k].x >> 16), a.d, u);
+                w.z = apply_elem(w.z, bf16_to_f32(ov[k].y & 0xffffu), a.d, u);
+                w.w = apply_elem(w.w, bf16_to_f32(ov[k].y >> 16), a.d, u);
+                *reinterpret_cast<float4*>(e.w + idx) = w;
+            }
+            continue;
+        }
+        // Interior tile: all loads first (see the momentum kernel).
+        const bool full = vec && r0 + T <= e.rows && c0 + T <= e.cols && (a.np & 3) == 0;
+        if (full) {
+            float4 wv[4];
+            uint2 ov[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = r0 + rg + 16 * i;
+                wv[i] = *reinterpret_cast<const float4*>(e.w + r * e.cols + c);
+                if (!e.trans) ov[i] = *reinterpret_cast<const uint2*>(O + r * a.np + c);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t r = r0 + rg + 16 * i;
+                float o[4];
+                if (e.trans) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = bf16_to_f32(tr[cg * 4 + j][rg + 16 * i]);
+                } else {
+                    o[0] = bf16_to_f32(ov[i].x & 0xffffu); o[1] = bf16_to_f32(ov[i].x >> 16);
+                    o[2] = bf16_to_f32(ov[i].y & 0xffffu); o[3] = bf16_to_f32(ov[i].y >> 16);
+                }
+                float4 w = wv[i];
+                w.x = apply_elem(w.x, o[0], a.d, u);
+                w.y = apply_elem(w.y, o[1], a.d, u);
+                w.z = apply_elem(w.z, o[2], a.d, u);
+                w.w = apply_elem(w.w, o[3], a.d, u);
+                *reinterpret_cast<float4*>(e.w + r * e.cols + c) = w;
+            }
+        }
+
+#pragma unroll
+        for (int i = 0; i < 4 && !full; ++i) {
             const int64_t r = r0 + rg + 16 * i;
             if (r >= e.rows || c >= e.cols) continue;
             const int64_t base = r * e.cols + c;
@@ -294,7 +456,7 @@ hipError_t launch_finalize(const FinalizeArgs& a, int64_t count, hipStream_t s) 
 }
 
 hipError_t launch_normalize(const NormalizeArgs& a, hipStream_t s) {
-    const unsigned grid = grid_for((a.total_units + 255) / 256, 256 * 16);
+    const unsigned grid = grid_for((a.total_units + 256 * UPT - 1) / (256 * UPT), 256 * 16);
     hipLaunchKernelGGL(normalize_kernel, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
