@@ -76,6 +76,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle leg (profiling runs)")
+    ap.add_argument("--max-workspace-gib", type=float, default=-1.0,
+                    help="workspace cap in GiB (0: none; default: none if it fits next to the inputs, "
+                         "else 8 GiB chunks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -120,7 +123,19 @@ def main(argv=None):
                 snap[i] = tuple(t.detach().float().cpu().numpy() if t.dtype == torch.bfloat16 else
                                 t.detach().cpu().numpy() for t in (params[i].weight, params[i].momentum, params[i].grad))
 
-    plan = harness.Plan(params)
+    # Workspace: the whole plan if it fits in the memory the inputs leave, otherwise
+    # chunks that share one region of a few GiB (the moe_slice workload: 261 GB of inputs).
+    cap = 0
+    if args.max_workspace_gib >= 0:
+        cap = int(args.max_workspace_gib * (1 << 30))
+    else:
+        probe = harness.Plan(params, bind=False)
+        need = probe.workspace_bytes
+        probe.close()
+        free, _ = torch.cuda.mem_get_info()
+        if need > free - (4 << 30):
+            cap = 8 << 30
+    plan = harness.Plan(params, max_workspace_bytes=cap)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -255,6 +270,7 @@ def main(argv=None):
         "config": {
             "workload": w.key, "description": w.description,
             "matrices": len(w.matrices), "buckets": plan.n_buckets, "chunks": plan.n_chunks,
+            "workspace_gib": round(plan.workspace_bytes / (1 << 30), 3),
             "ns_iterations": w.steps, "coefficients": [w.a, w.b, w.c], "beta": w.beta,
             "lr": w.lr, "wd": w.wd, "parallelism": "single GPU",
         },
