@@ -91,7 +91,23 @@ typedef struct muon_plan_opts {
     const float* scale;
     /* MUON_PLAN_* bits; 0 for the defaults. */
     uint32_t flags;
+    /* Update-scale rule used where `scale` is NULL (MUON_SCALE_*).  The pages give no
+     * rule: one of them notes only that careful per-parameter scaling of the update
+     * was a key to scaling Muon, in the prior work it names ("MAI-Base-2 в 4–12 раз
+     * экономнее DeepSeek на предобучении", section "Muon обошёл AdamW, но потребовал
+     * пересобирать матрицы между GPU"). */
+    int32_t scale_mode;
 } muon_plan_opts;
+
+/* s_i = 1. */
+#define MUON_SCALE_NONE 0
+/* s_i = sqrt(max(1, rows / cols)) of the parameter as stored (rows = outputs): the
+ * scale of the original Muon write-up, which keeps tall matrices' per-element update
+ * size in line with square ones. */
+#define MUON_SCALE_ASPECT 1
+/* s_i = 0.2 * sqrt(max(rows, cols)): gives the orthogonalised update an RMS of about
+ * 0.2, the range of AdamW's updates (the rule of Moonshot AI's Muon scaling paper). */
+#define MUON_SCALE_RMS_MATCH 2
 
 /* Orthogonalise small matrices with the tiled kernels too, instead of the fused
  * whole-iteration kernel (both give bitwise the same result; this exists to show it). */
@@ -124,7 +140,7 @@ typedef struct muon_param_info {
     int32_t chunk;
     int64_t slot;           /* index of the matrix inside its chunk                   */
     int32_t transposed;     /* 1 when rows > cols: O is stored as the m x n transpose */
-    int32_t reserved;
+    float scale;            /* the update scale s_i the apply step uses               */
     uint64_t output_offset; /* byte offset of O (bf16, m x n, row stride ld) in the workspace */
     int64_t ld;             /* row stride of O in elements (= n_pad)                  */
 } muon_param_info;
@@ -198,6 +214,44 @@ MUON_API muon_status muon_apply(const muon_plan* plan, int32_t chunk, float lr, 
 MUON_API muon_status muon_step(const muon_plan* plan, int32_t chunk, float beta, float a, float b,
                       float c, int32_t steps, float eps, float lr, float wd, void* stream);
 
+/* ---- variants the pages leave open ------------------------------------------------------ */
+
+/* Step 3 with its own coefficients per iteration: `coeffs` (host) holds 3*steps floats
+ * (a_t, b_t, c_t), t = 1..steps; iteration t runs A = X X^T, B = b_t A + c_t A A,
+ * X = a_t X + B X.  The pages fix neither the coefficients nor their schedule;
+ * muon_ns_batched is this call with the same (a, b, c) every iteration.
+ * Errors: INVALID_ARG (chunk, coeffs NULL, steps outside [1, 1024], non-finite values,
+ * eps < 0), NOT_BOUND, HIP. */
+MUON_API muon_status muon_ns_batched_schedule(const muon_plan* plan, int32_t chunk, const float* coeffs,
+                                     int32_t steps, float eps, void* stream);
+
+/* Everything one step takes, for muon_step_ex and muon_graph_capture_ex. */
+typedef struct muon_step_config {
+    float beta;                /* momentum coefficient                                     */
+    float lr, wd;              /* learning rate, decoupled weight decay                    */
+    float eps;                 /* added to the Frobenius norm (>= 0)                       */
+    int32_t steps;             /* Newton–Schulz iterations, 1..1024                        */
+    float a, b, c;             /* each iteration's coefficients when `coeffs` is NULL      */
+    const float* coeffs;       /* host, nullable: 3*steps floats (a_t, b_t, c_t)           */
+    /* 0: Newton–Schulz takes bf16(M_new), the momentum itself (the pages' step 1).
+     * 1: it takes the Nesterov look-ahead bf16(f32(beta*M_new + (1-beta)*G)), formed like
+     *    the momentum (float64 products and sum, one float32 rounding).  The stored
+     *    momentum is M_new either way. */
+    int32_t nesterov;
+    /* Device, nullable, 4-byte aligned: {beta, lr, wd} as three floats, read by the
+     * kernels when they run instead of the fields above (whose values are then
+     * ignored).  A captured graph then follows a learning-rate or decay schedule: write
+     * the new values into this buffer, ordered before each launch.  Non-finite values
+     * are not checked; they propagate as data. */
+    const float* dev_scalars;
+} muon_step_config;
+
+/* muon_step with a muon_step_config.  Errors: INVALID_ARG (NULL config, chunk, steps,
+ * non-finite scalars or coefficients, nesterov not 0/1), ALIGNMENT (dev_scalars),
+ * NOT_BOUND, HIP. */
+MUON_API muon_status muon_step_ex(const muon_plan* plan, int32_t chunk, const muon_step_config* config,
+                         void* stream);
+
 /* ---- the whole step as one graph ------------------------------------------------------- */
 
 /* The pages count kernel-dispatch overhead among the causes of the gap between the
@@ -218,6 +272,9 @@ MUON_API muon_status muon_step(const muon_plan* plan, int32_t chunk, float beta,
 typedef struct muon_graph muon_graph;
 MUON_API muon_status muon_graph_capture(const muon_plan* plan, float beta, float a, float b, float c,
                                int32_t steps, float eps, float lr, float wd, muon_graph** out);
+/* muon_graph_capture with a muon_step_config (schedules, Nesterov, device scalars). */
+MUON_API muon_status muon_graph_capture_ex(const muon_plan* plan, const muon_step_config* config,
+                                  muon_graph** out);
 /* Launch one step, ordered on `stream` (the null stream is allowed).  Launches of one
  * graph, or of graphs of one plan, must not overlap on different streams. */
 MUON_API muon_status muon_graph_launch(const muon_graph* graph, void* stream);

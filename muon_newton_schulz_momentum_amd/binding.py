@@ -48,6 +48,10 @@ MUON_KERNEL_COUNT = 8
 
 MUON_PLAN_TILED_SMALL = 1
 
+MUON_SCALE_NONE = 0
+MUON_SCALE_ASPECT = 1
+MUON_SCALE_RMS_MATCH = 2
+
 
 class muon_param_desc(C.Structure):
     _fields_ = [("ndim", C.c_int32), ("grad_dtype", C.c_int32), ("rows", C.c_int64),
@@ -56,7 +60,8 @@ class muon_param_desc(C.Structure):
 
 
 class muon_plan_opts(C.Structure):
-    _fields_ = [("max_workspace_bytes", C.c_uint64), ("scale", C.POINTER(C.c_float)), ("flags", C.c_uint32)]
+    _fields_ = [("max_workspace_bytes", C.c_uint64), ("scale", C.POINTER(C.c_float)), ("flags", C.c_uint32),
+                ("scale_mode", C.c_int32)]
 
 
 class muon_chunk_info(C.Structure):
@@ -69,9 +74,15 @@ class muon_chunk_info(C.Structure):
                 ("region_offset", C.c_uint64), ("region_bytes", C.c_uint64)]
 
 
+class muon_step_config(C.Structure):
+    _fields_ = [("beta", C.c_float), ("lr", C.c_float), ("wd", C.c_float), ("eps", C.c_float),
+                ("steps", C.c_int32), ("a", C.c_float), ("b", C.c_float), ("c", C.c_float),
+                ("coeffs", C.POINTER(C.c_float)), ("nesterov", C.c_int32), ("dev_scalars", C.c_void_p)]
+
+
 class muon_param_info(C.Structure):
     _fields_ = [("included", C.c_int32), ("chunk", C.c_int32), ("slot", C.c_int64),
-                ("transposed", C.c_int32), ("reserved", C.c_int32),
+                ("transposed", C.c_int32), ("scale", C.c_float),
                 ("output_offset", C.c_uint64), ("ld", C.c_int64)]
 
 
@@ -99,6 +110,9 @@ muon_momentum_update = _fn("muon_momentum_update", C.c_int32, [_P, C.c_int32, C.
 muon_ns_batched = _fn("muon_ns_batched", C.c_int32,
                       [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float, C.c_void_p])
 muon_apply = _fn("muon_apply", C.c_int32, [_P, C.c_int32, C.c_float, C.c_float, C.c_void_p])
+muon_ns_batched_schedule = _fn("muon_ns_batched_schedule", C.c_int32,
+                               [_P, C.c_int32, C.POINTER(C.c_float), C.c_int32, C.c_float, C.c_void_p])
+muon_step_ex = _fn("muon_step_ex", C.c_int32, [_P, C.c_int32, C.POINTER(muon_step_config), C.c_void_p])
 muon_step = _fn("muon_step", C.c_int32,
                 [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float,
                  C.c_float, C.c_float, C.c_void_p])
@@ -106,6 +120,7 @@ _G = C.c_void_p  # muon_graph*
 muon_graph_capture = _fn("muon_graph_capture", C.c_int32,
                          [_P, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float, C.c_float,
                           C.c_float, C.POINTER(_G)])
+muon_graph_capture_ex = _fn("muon_graph_capture_ex", C.c_int32, [_P, C.POINTER(muon_step_config), C.POINTER(_G)])
 muon_graph_launch = _fn("muon_graph_launch", C.c_int32, [_G, C.c_void_p])
 muon_graph_node_count = _fn("muon_graph_node_count", C.c_int32, [_G, C.POINTER(C.c_int64)])
 muon_graph_destroy = _fn("muon_graph_destroy", None, [_G])
@@ -121,7 +136,8 @@ muon_last_error = _fn("muon_last_error", C.c_char_p, [])
 EXPORTED = [
     "muon_plan_buckets", "muon_plan_workspace_bytes", "muon_plan_counts", "muon_plan_info",
     "muon_plan_param_info", "muon_plan_validate", "muon_plan_bind", "muon_momentum_update",
-    "muon_ns_batched", "muon_apply", "muon_step", "muon_graph_capture", "muon_graph_launch",
+    "muon_ns_batched", "muon_ns_batched_schedule", "muon_apply", "muon_step", "muon_step_ex",
+    "muon_graph_capture", "muon_graph_capture_ex", "muon_graph_launch",
     "muon_graph_node_count", "muon_graph_destroy", "muon_timing_enable", "muon_timing_read",
     "muon_timing_reset", "muon_kernel_name", "muon_plan_destroy", "muon_status_string",
     "muon_last_error",

@@ -58,9 +58,41 @@ struct TimedLaunch {
     }
 };
 
+// ---- one step's settings ----------------------------------------------------------------
+
+struct StepCfg {
+    float beta = 0.f, lr = 0.f, wd = 0.f, eps = 0.f;
+    int32_t steps = 0;
+    std::vector<float> abc;          // (a, b, c) of each iteration, 3 * steps values
+    bool nesterov = false;
+    const float* dev = nullptr;      // device {beta, lr, wd}, read by the kernels when set
+};
+
+void fill_abc(StepCfg& cfg, float a, float b, float c) {
+    cfg.abc.resize(3 * (size_t)cfg.steps);
+    for (int32_t t = 0; t < cfg.steps; ++t) {
+        cfg.abc[3 * (size_t)t] = a;
+        cfg.abc[3 * (size_t)t + 1] = b;
+        cfg.abc[3 * (size_t)t + 2] = c;
+    }
+}
+
+bool finite(float v) { return std::isfinite(v); }
+
+constexpr int32_t MAX_NS_STEPS = 1024;
+
+muon_status check_ns(int32_t steps, const float* abc, float eps, const char* who) {
+    if (steps < 1 || steps > MAX_NS_STEPS)
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": steps must be in [1, 1024]");
+    if (!finite(eps) || eps < 0.f) return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": eps must be finite and >= 0");
+    for (int32_t i = 0; i < 3 * steps; ++i)
+        if (!finite(abc[i])) return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": coefficients must be finite");
+    return MUON_OK;
+}
+
 // ---- the three steps for one chunk --------------------------------------------------------
 
-muon_status momentum_chunk(const muon_plan* p, const Chunk& c, float beta, hipStream_t s) {
+muon_status momentum_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, hipStream_t s) {
     MomentumArgs a;
     a.tbl = at<const MatEntry>(p, c.off_table);
     a.xq = at<uint16_t>(p, c.off_xq);
@@ -69,8 +101,10 @@ muon_status momentum_chunk(const muon_plan* p, const Chunk& c, float beta, hipSt
     a.np = c.np;
     a.ew_tiles = c.ew_tiles;
     a.total_tiles = c.count * c.ew_tiles;
-    a.beta = beta;
-    a.omb = 1.0f - beta;
+    a.beta = cfg.beta;
+    a.omb = 1.0f - cfg.beta;
+    a.dev_scalars = cfg.dev;
+    a.nesterov = cfg.nesterov ? 1 : 0;
     const double gsz = c.grad_dtype == MUON_DTYPE_F32 ? 4.0 : 2.0;
     TimedLaunch tl(p, MUON_KERNEL_MOMENTUM, (double)c.count * c.m * c.n * (10.0 + gsz), s);
     const hipError_t e = launch_momentum(a, c.grad_dtype, s);
@@ -78,8 +112,8 @@ muon_status momentum_chunk(const muon_plan* p, const Chunk& c, float beta, hipSt
     return e == hipSuccess ? MUON_OK : hip_fail(e, "momentum kernel launch");
 }
 
-muon_status ns_chunk(const muon_plan* p, const Chunk& c, float a_, float b_, float c_, int32_t steps,
-                     float eps, hipStream_t s) {
+muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, float eps,
+                     hipStream_t s) {
     uint16_t* xp = at<uint16_t>(p, c.off_xp);
     uint16_t* xq = at<uint16_t>(p, c.off_xq);
     uint16_t* am = at<uint16_t>(p, c.off_a);
@@ -112,6 +146,7 @@ muon_status ns_chunk(const muon_plan* p, const Chunk& c, float a_, float b_, flo
     const double m = (double)c.m, n = (double)c.n, cnt = (double)c.count;
 
     for (int32_t it = 0; it < steps; ++it) {
+        const float a_ = abc[3 * it], b_ = abc[3 * it + 1], c_ = abc[3 * it + 2];
         uint16_t* nxt = (cur == xp) ? xq : xp;
         NsArgs g{};
         // A = X X^T
@@ -163,9 +198,17 @@ double ns_iter_flops(const Chunk& c) {
 
 // The fused small-matrix kernel over the given chunks (all with Chunk::fused), in
 // launches of up to SMALL_NS_MAX_JOBS chunks: normaliser, normalisation and every
-// iteration in one launch.
-muon_status ns_small_chunks(const muon_plan* p, const std::vector<int32_t>& idx, float a_, float b_, float c_,
-                            int32_t steps, float eps, hipStream_t s) {
+// iteration in one launch.  A schedule longer than the kernel's coefficient table goes
+// through the tiled kernels instead (bitwise the same result).
+muon_status ns_small_chunks(const muon_plan* p, const std::vector<int32_t>& idx, const float* abc, int32_t steps,
+                            float eps, hipStream_t s) {
+    if (steps > SMALL_NS_MAX_STEPS) {
+        for (int32_t i : idx) {
+            const muon_status st = ns_chunk(p, p->chunks[(size_t)i], abc, steps, eps, s);
+            if (st != MUON_OK) return st;
+        }
+        return MUON_OK;
+    }
     for (size_t g0 = 0; g0 < idx.size(); g0 += SMALL_NS_MAX_JOBS) {
         SmallNsArgs A{};
         int64_t total = 0;
@@ -185,9 +228,8 @@ muon_status ns_small_chunks(const muon_plan* p, const std::vector<int32_t>& idx,
             work += steps * ns_iter_flops(ch);
         }
         A.steps = steps;
-        A.a = a_;
-        A.b = b_;
-        A.c = c_;
+        for (int32_t t = 0; t < steps; ++t)
+            for (int32_t q = 0; q < 3; ++q) A.abc[t][q] = abc[3 * t + q];
         A.eps = (double)eps;
         TimedLaunch tl(p, MUON_KERNEL_NS_SMALL, work, s);
         const hipError_t e = launch_ns_small(A, total, s);
@@ -198,29 +240,28 @@ muon_status ns_small_chunks(const muon_plan* p, const std::vector<int32_t>& idx,
 }
 
 // Newton–Schulz for one chunk, by whichever path the plan chose for it.
-muon_status ns_one(const muon_plan* p, int32_t i, float a_, float b_, float c_, int32_t steps, float eps,
-                   hipStream_t s) {
+muon_status ns_one(const muon_plan* p, int32_t i, const float* abc, int32_t steps, float eps, hipStream_t s) {
     const Chunk& ch = p->chunks[(size_t)i];
-    if (ch.fused) return ns_small_chunks(p, std::vector<int32_t>{i}, a_, b_, c_, steps, eps, s);
-    return ns_chunk(p, ch, a_, b_, c_, steps, eps, s);
+    if (ch.fused) return ns_small_chunks(p, std::vector<int32_t>{i}, abc, steps, eps, s);
+    return ns_chunk(p, ch, abc, steps, eps, s);
 }
 
 // Newton–Schulz for every chunk (their regions are distinct): all fused chunks in grouped
 // launches, then the tiled ones.
-muon_status ns_all(const muon_plan* p, float a_, float b_, float c_, int32_t steps, float eps, hipStream_t s) {
+muon_status ns_all(const muon_plan* p, const float* abc, int32_t steps, float eps, hipStream_t s) {
     std::vector<int32_t> small;
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
         if (p->chunks[(size_t)i].fused) small.push_back(i);
-    muon_status st = ns_small_chunks(p, small, a_, b_, c_, steps, eps, s);
+    muon_status st = ns_small_chunks(p, small, abc, steps, eps, s);
     if (st != MUON_OK) return st;
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
         const Chunk& ch = p->chunks[(size_t)i];
-        if (!ch.fused && (st = ns_chunk(p, ch, a_, b_, c_, steps, eps, s)) != MUON_OK) return st;
+        if (!ch.fused && (st = ns_chunk(p, ch, abc, steps, eps, s)) != MUON_OK) return st;
     }
     return MUON_OK;
 }
 
-muon_status apply_chunk(const muon_plan* p, const Chunk& c, float lr, float wd, hipStream_t s) {
+muon_status apply_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, hipStream_t s) {
     ApplyArgs a;
     a.tbl = at<const MatEntry>(p, c.off_table);
     a.xo = at<const uint16_t>(p, c.off_xp);
@@ -228,48 +269,71 @@ muon_status apply_chunk(const muon_plan* p, const Chunk& c, float lr, float wd, 
     a.np = c.np;
     a.ew_tiles = c.ew_tiles;
     a.total_tiles = c.count * c.ew_tiles;
-    const double lw = (double)lr * (double)wd;   // exact
-    a.d = 1.0 - lw;                               // one float64 rounding
-    a.lr = lr;
+    const double lw = (double)cfg.lr * (double)cfg.wd;   // exact
+    a.d = 1.0 - lw;                                       // one float64 rounding
+    a.lr = cfg.lr;
+    a.dev_scalars = cfg.dev;
     TimedLaunch tl(p, MUON_KERNEL_APPLY, (double)c.count * c.m * c.n * 10.0, s);
     const hipError_t e = launch_apply(a, s);
     tl.done(s);
     return e == hipSuccess ? MUON_OK : hip_fail(e, "apply kernel launch");
 }
 
-bool finite(float v) { return std::isfinite(v); }
-
 // Steps 1, 3 and 5 for one chunk, or for every chunk (-1) on one stream.  With distinct
 // regions every chunk's momentum runs first, then Newton–Schulz (small chunks grouped),
 // then every apply; chunks that share a region go through all three in turn.
-muon_status step_chunks(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,
-                        float eps, float lr, float wd, hipStream_t s) {
+muon_status step_chunks(const muon_plan* p, int32_t chunk, const StepCfg& cfg, hipStream_t s) {
     muon_status st;
     const int32_t nc = (int32_t)p->chunks.size();
+    const float* abc = cfg.abc.data();
     if (chunk == -1 && !p->shared_regions) {
         for (int32_t i = 0; i < nc; ++i)
-            if ((st = momentum_chunk(p, p->chunks[(size_t)i], beta, s)) != MUON_OK) return st;
-        if ((st = ns_all(p, a, b, c, steps, eps, s)) != MUON_OK) return st;
+            if ((st = momentum_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
+        if ((st = ns_all(p, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
         for (int32_t i = 0; i < nc; ++i)
-            if ((st = apply_chunk(p, p->chunks[(size_t)i], lr, wd, s)) != MUON_OK) return st;
+            if ((st = apply_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
         return MUON_OK;
     }
     for (int32_t i = 0; i < nc; ++i) {
         if (chunk != -1 && i != chunk) continue;
         const Chunk& ch = p->chunks[(size_t)i];
-        if ((st = momentum_chunk(p, ch, beta, s)) != MUON_OK) return st;
-        if ((st = ns_one(p, i, a, b, c, steps, eps, s)) != MUON_OK) return st;
-        if ((st = apply_chunk(p, ch, lr, wd, s)) != MUON_OK) return st;
+        if ((st = momentum_chunk(p, ch, cfg, s)) != MUON_OK) return st;
+        if ((st = ns_one(p, i, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+        if ((st = apply_chunk(p, ch, cfg, s)) != MUON_OK) return st;
     }
     return MUON_OK;
 }
 
-muon_status check_step_scalars(float beta, float a, float b, float c, int32_t steps, float eps, float lr, float wd,
-                               const char* who) {
-    if (!finite(beta) || !finite(lr) || !finite(wd) || !finite(a) || !finite(b) || !finite(c) || !finite(eps) ||
-        eps < 0.f || steps < 1)
-        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": scalars must be finite, eps >= 0 and steps >= 1");
+// A StepCfg from the public config (validated).
+muon_status make_cfg(const muon_step_config* c, StepCfg& cfg, const char* who) {
+    if (!c) return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": config is NULL");
+    cfg.steps = c->steps;
+    if (c->steps < 1 || c->steps > MAX_NS_STEPS)
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": steps must be in [1, 1024]");
+    if (c->coeffs) cfg.abc.assign(c->coeffs, c->coeffs + 3 * (size_t)c->steps);
+    else fill_abc(cfg, c->a, c->b, c->c);
+    muon_status st = check_ns(cfg.steps, cfg.abc.data(), c->eps, who);
+    if (st != MUON_OK) return st;
+    if (c->nesterov != 0 && c->nesterov != 1)
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": nesterov must be 0 or 1");
+    if (!c->dev_scalars && (!finite(c->beta) || !finite(c->lr) || !finite(c->wd)))
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": beta, lr and wd must be finite");
+    if (c->dev_scalars && ((uintptr_t)c->dev_scalars & 3u) != 0)
+        return set_error(MUON_ERR_ALIGNMENT, std::string(who) + ": dev_scalars must be 4-byte aligned");
+    cfg.beta = c->beta;
+    cfg.lr = c->lr;
+    cfg.wd = c->wd;
+    cfg.eps = c->eps;
+    cfg.nesterov = c->nesterov == 1;
+    cfg.dev = c->dev_scalars;
     return MUON_OK;
+}
+
+muon_step_config legacy_config(float beta, float a, float b, float c, int32_t steps, float eps, float lr, float wd) {
+    muon_step_config k{};
+    k.beta = beta; k.lr = lr; k.wd = wd; k.eps = eps; k.steps = steps;
+    k.a = a; k.b = b; k.c = c;
+    return k;
 }
 
 // The tile grid of a chunk must fit the kernels' int32 indexing, and one padded matrix
@@ -323,12 +387,28 @@ muon_status muon_momentum_update(const muon_plan* p, int32_t chunk, float beta, 
     muon_status st = check_step(p, chunk, "muon_momentum_update");
     if (st != MUON_OK) return st;
     if (!finite(beta)) return set_error(MUON_ERR_INVALID_ARG, "muon_momentum_update: beta must be finite");
+    StepCfg cfg;
+    cfg.beta = beta;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
         if (chunk != -1 && i != chunk) continue;
-        if ((st = momentum_chunk(p, p->chunks[(size_t)i], beta, s)) != MUON_OK) return st;
+        if ((st = momentum_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
     }
     return MUON_OK;
+}
+
+muon_status muon_ns_batched_schedule(const muon_plan* p, int32_t chunk, const float* coeffs, int32_t steps,
+                                     float eps, void* stream) {
+    clear_error();
+    muon_status st = check_step(p, chunk, "muon_ns_batched_schedule");
+    if (st != MUON_OK) return st;
+    if (!coeffs) return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched_schedule: coeffs is NULL");
+    if (steps < 1 || steps > MAX_NS_STEPS)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched_schedule: steps must be in [1, 1024]");
+    if ((st = check_ns(steps, coeffs, eps, "muon_ns_batched_schedule")) != MUON_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (chunk == -1) return ns_all(p, coeffs, steps, eps, s);
+    return ns_one(p, chunk, coeffs, steps, eps, s);
 }
 
 muon_status muon_ns_batched(const muon_plan* p, int32_t chunk, float a, float b, float c, int32_t steps,
@@ -336,12 +416,15 @@ muon_status muon_ns_batched(const muon_plan* p, int32_t chunk, float a, float b,
     clear_error();
     muon_status st = check_step(p, chunk, "muon_ns_batched");
     if (st != MUON_OK) return st;
-    if (steps < 1) return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched: steps must be >= 1");
-    if (!finite(a) || !finite(b) || !finite(c) || !finite(eps) || eps < 0.f)
-        return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched: coefficients must be finite and eps >= 0");
+    if (steps < 1 || steps > MAX_NS_STEPS)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched: steps must be in [1, 1024]");
+    StepCfg cfg;
+    cfg.steps = steps;
+    fill_abc(cfg, a, b, c);
+    if ((st = check_ns(steps, cfg.abc.data(), eps, "muon_ns_batched")) != MUON_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (chunk == -1) return ns_all(p, a, b, c, steps, eps, s);
-    return ns_one(p, chunk, a, b, c, steps, eps, s);
+    if (chunk == -1) return ns_all(p, cfg.abc.data(), steps, eps, s);
+    return ns_one(p, chunk, cfg.abc.data(), steps, eps, s);
 }
 
 muon_status muon_apply(const muon_plan* p, int32_t chunk, float lr, float wd, void* stream) {
@@ -349,36 +432,45 @@ muon_status muon_apply(const muon_plan* p, int32_t chunk, float lr, float wd, vo
     muon_status st = check_step(p, chunk, "muon_apply");
     if (st != MUON_OK) return st;
     if (!finite(lr) || !finite(wd)) return set_error(MUON_ERR_INVALID_ARG, "muon_apply: lr and wd must be finite");
+    StepCfg cfg;
+    cfg.lr = lr;
+    cfg.wd = wd;
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
         if (chunk != -1 && i != chunk) continue;
-        if ((st = apply_chunk(p, p->chunks[(size_t)i], lr, wd, s)) != MUON_OK) return st;
+        if ((st = apply_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
     }
     return MUON_OK;
 }
 
+muon_status muon_step_ex(const muon_plan* p, int32_t chunk, const muon_step_config* config, void* stream) {
+    clear_error();
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_step_ex: plan is NULL");
+    if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_step_ex: call muon_plan_bind first");
+    if (chunk < -1 || chunk >= (int32_t)p->chunks.size())
+        return set_error(MUON_ERR_INVALID_ARG, "muon_step_ex: chunk out of range");
+    StepCfg cfg;
+    muon_status st = make_cfg(config, cfg, "muon_step_ex");
+    if (st != MUON_OK) return st;
+    return step_chunks(p, chunk, cfg, static_cast<hipStream_t>(stream));
+}
+
 muon_status muon_step(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,
                       float eps, float lr, float wd, void* stream) {
-    clear_error();
-    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_step: plan is NULL");
-    if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_step: call muon_plan_bind first");
-    if (chunk < -1 || chunk >= (int32_t)p->chunks.size())
-        return set_error(MUON_ERR_INVALID_ARG, "muon_step: chunk out of range");
-    muon_status st = check_step_scalars(beta, a, b, c, steps, eps, lr, wd, "muon_step");
-    if (st != MUON_OK) return st;
-    return step_chunks(p, chunk, beta, a, b, c, steps, eps, lr, wd, static_cast<hipStream_t>(stream));
+    const muon_step_config k = legacy_config(beta, a, b, c, steps, eps, lr, wd);
+    return muon_step_ex(p, chunk, &k, stream);
 }
 
 // ---- the step as one graph ----------------------------------------------------------------
 
-muon_status muon_graph_capture(const muon_plan* p, float beta, float a, float b, float c, int32_t steps, float eps,
-                               float lr, float wd, muon_graph** out) {
+muon_status muon_graph_capture_ex(const muon_plan* p, const muon_step_config* config, muon_graph** out) {
     clear_error();
     if (!out) return set_error(MUON_ERR_INVALID_ARG, "muon_graph_capture: out is NULL");
     *out = nullptr;
     if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_graph_capture: plan is NULL");
     if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_graph_capture: call muon_plan_bind first");
-    muon_status st = check_step_scalars(beta, a, b, c, steps, eps, lr, wd, "muon_graph_capture");
+    StepCfg cfg;
+    muon_status st = make_cfg(config, cfg, "muon_graph_capture");
     if (st != MUON_OK) return st;
 
     // A private stream: the caller's stream may be the null stream, which cannot capture.
@@ -392,7 +484,7 @@ muon_status muon_graph_capture(const muon_plan* p, float beta, float a, float b,
         return hip_fail(e, "muon_graph_capture: hipStreamBeginCapture");
     }
     t_capturing = true;
-    st = step_chunks(p, -1, beta, a, b, c, steps, eps, lr, wd, cs);
+    st = step_chunks(p, -1, cfg, cs);
     t_capturing = false;
     const std::string launch_error = st == MUON_OK ? std::string() : std::string(muon_last_error());
     e = hipStreamEndCapture(cs, &graph);
@@ -420,6 +512,12 @@ muon_status muon_graph_capture(const muon_plan* p, float beta, float a, float b,
     g->ws = p->ws;
     *out = g;
     return MUON_OK;
+}
+
+muon_status muon_graph_capture(const muon_plan* p, float beta, float a, float b, float c, int32_t steps, float eps,
+                               float lr, float wd, muon_graph** out) {
+    const muon_step_config k = legacy_config(beta, a, b, c, steps, eps, lr, wd);
+    return muon_graph_capture_ex(p, &k, out);
 }
 
 muon_status muon_graph_launch(const muon_graph* g, void* stream) {

@@ -53,13 +53,26 @@ __device__ __forceinline__ float momentum_elem(float m, float g, double beta, do
     return (float)(p1 + p2);              // one float64 rounding, then one float32 rounding
 }
 
+// The bf16 matrix handed to Newton–Schulz: the new momentum itself, or with Nesterov the
+// look-ahead beta*M_new + (1-beta)*G, formed exactly like the momentum (float64 products
+// and sum, one float32 rounding) and then cast.
+__device__ __forceinline__ uint16_t x0_bits(float mn, float g, bool nesterov, double beta, double omb) {
+    return f32_to_bf16(nesterov ? momentum_elem(mn, g, beta, omb) : mn);
+}
+
 template <int GDT>
 __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tr[T][LDT];
     __shared__ double red[4];
     const int tid = threadIdx.x;
     const int cg = tid & 15, rg = tid >> 4;
-    const double beta = (double)a.beta, omb = (double)a.omb;
+    float beta32 = a.beta, omb32 = a.omb;
+    if (a.dev_scalars) {            // beta from device memory; (1 - beta) formed as the host forms it
+        beta32 = a.dev_scalars[0];
+        omb32 = 1.0f - beta32;
+    }
+    const double beta = (double)beta32, omb = (double)omb32;
+    const bool nest = a.nesterov != 0;
 
     for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int64_t mat = t / a.ew_tiles;
@@ -100,7 +113,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
                 mn.z = momentum_elem(mv[k].z, gv[k][2], beta, omb);
                 mn.w = momentum_elem(mv[k].w, gv[k][3], beta, omb);
                 *reinterpret_cast<float4*>(e.m + idx) = mn;
-                const uint16_t xb[4] = {f32_to_bf16(mn.x), f32_to_bf16(mn.y), f32_to_bf16(mn.z), f32_to_bf16(mn.w)};
+                const uint16_t xb[4] = {x0_bits(mn.x, gv[k][0], nest, beta, omb), x0_bits(mn.y, gv[k][1], nest, beta, omb),
+                                        x0_bits(mn.z, gv[k][2], nest, beta, omb), x0_bits(mn.w, gv[k][3], nest, beta, omb)};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const double x = (double)bf16_to_f32(xb[j]);
@@ -137,7 +151,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
                 mn.z = momentum_elem(mv[i].z, gv[i][2], beta, omb);
                 mn.w = momentum_elem(mv[i].w, gv[i][3], beta, omb);
                 *reinterpret_cast<float4*>(e.m + base) = mn;
-                const uint16_t xb[4] = {f32_to_bf16(mn.x), f32_to_bf16(mn.y), f32_to_bf16(mn.z), f32_to_bf16(mn.w)};
+                const uint16_t xb[4] = {x0_bits(mn.x, gv[i][0], nest, beta, omb), x0_bits(mn.y, gv[i][1], nest, beta, omb),
+                                        x0_bits(mn.z, gv[i][2], nest, beta, omb), x0_bits(mn.w, gv[i][3], nest, beta, omb)};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const double x = (double)bf16_to_f32(xb[j]);
@@ -173,14 +188,15 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
                     mn.z = momentum_elem(mv.z, gv[2], beta, omb);
                     mn.w = momentum_elem(mv.w, gv[3], beta, omb);
                     *reinterpret_cast<float4*>(e.m + base) = mn;
-                    xb[0] = f32_to_bf16(mn.x); xb[1] = f32_to_bf16(mn.y);
-                    xb[2] = f32_to_bf16(mn.z); xb[3] = f32_to_bf16(mn.w);
+                    xb[0] = x0_bits(mn.x, gv[0], nest, beta, omb); xb[1] = x0_bits(mn.y, gv[1], nest, beta, omb);
+                    xb[2] = x0_bits(mn.z, gv[2], nest, beta, omb); xb[3] = x0_bits(mn.w, gv[3], nest, beta, omb);
                 } else {
                     nvalid = (int)((e.cols - c) < 4 ? (e.cols - c) : 4);
                     for (int j = 0; j < nvalid; ++j) {
-                        const float mn = momentum_elem(e.m[base + j], load_grad1<GDT>(e.g, base + j), beta, omb);
+                        const float gj = load_grad1<GDT>(e.g, base + j);
+                        const float mn = momentum_elem(e.m[base + j], gj, beta, omb);
                         e.m[base + j] = mn;
-                        xb[j] = f32_to_bf16(mn);
+                        xb[j] = x0_bits(mn, gj, nest, beta, omb);
                     }
                 }
 #pragma unroll
@@ -313,6 +329,11 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tr[T][LDT];
     const int tid = threadIdx.x;
     const int cg = tid & 15, rg = tid >> 4;
+    if (a.dev_scalars) {            // lr and wd from device memory; d formed as the host forms it
+        const float lr = a.dev_scalars[1], wd = a.dev_scalars[2];
+        a.lr = lr;
+        a.d = 1.0 - (double)lr * (double)wd;
+    }
 
     for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
         const int64_t mat = t / a.ew_tiles;

@@ -18,6 +18,8 @@ struct MomentumArgs {
     int64_t ew_tiles;
     int64_t total_tiles;   // count * ew_tiles
     float beta, omb;       // beta and (1 - beta), both as the caller's float32
+    const float* dev_scalars;  // nullable device {beta, lr, wd}: beta is read from it instead
+    int32_t nesterov;      // 1: X0 = bf16(f32(beta*M_new + (1-beta)*G)) instead of bf16(M_new)
 };
 
 struct FinalizeArgs {
@@ -44,6 +46,7 @@ struct ApplyArgs {
     int64_t total_tiles;
     double d;              // 1 - lr*wd, formed in float64
     float lr;
+    const float* dev_scalars;  // nullable device {beta, lr, wd}: lr and wd are read from it instead
 };
 
 // Newton–Schulz GEMM kernels.  opa/opb are matrix-0 bases; every matrix of the chunk
@@ -71,6 +74,7 @@ struct NsArgs {
 // one workgroup per matrix; every job is one chunk of such matrices.
 
 constexpr int SMALL_NS_MAX_JOBS = 8;
+constexpr int SMALL_NS_MAX_STEPS = 32;   // longest coefficient schedule the fused kernel holds
 
 struct SmallJob {
     const uint16_t* xq;        // X0: count matrices of 64 x np bf16
@@ -85,7 +89,7 @@ struct SmallNsArgs {
     SmallJob job[SMALL_NS_MAX_JOBS];
     int32_t n_jobs;
     int32_t steps;
-    float a, b, c;
+    float abc[SMALL_NS_MAX_STEPS][3];   // (a, b, c) of each iteration
     double eps;
 };
 

@@ -9,7 +9,7 @@
 // workgroup takes one canonical m x n matrix with m <= 64 and n (padded) <= 1024, keeps X
 // (64 x n bf16), A and B (64 x 64 bf16 each) in 144 KB of LDS and runs
 //     inv = 1 / (||X0||_F + eps),  X = bf16(inv * X0),
-//     k times:  A = X X^T,  B = b A + c A A,  X = a X + B X,
+//     for t = 1..k:  A = X X^T,  B = b_t A + c_t A A,  X = a_t X + B X,
 // writing only the result.  All matrices of every small chunk of a plan go in one launch.
 //
 // Every product accumulates its 16-wide K slices in the same order as the tiled kernels
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void ns_small_kernel(SmallNsArgs a) {
         for (int v = 0; v < 16; ++v) {
             const int r = 32 * wi + 8 * (v >> 2) + 4 * kh + (v & 3);
             const float e = dev::bf16_to_f32(*reinterpret_cast<const uint16_t*>(Am + mb(r, 32 * wj + lr)));
-            const float val = dev::ns_combine(a.b, e, a.c, acc[v]);
+            const float val = dev::ns_combine(a.abc[it][1], e, a.abc[it][2], acc[v]);
             *reinterpret_cast<uint16_t*>(Bm + mb(r, 32 * wj + lr)) = dev::f32_to_bf16(val);
         }
         __syncthreads();
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void ns_small_kernel(SmallNsArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = 32 * h2 + 8 * (v >> 2) + 4 * kh + (v & 3);
-                    const float val = dev::ns_combine(a.a, e[h2][v], 1.f, acc2[h2][v]);
+                    const float val = dev::ns_combine(a.abc[it][0], e[h2][v], 1.f, acc2[h2][v]);
                     *reinterpret_cast<uint16_t*>(X + xb(r, n0 + lr)) = dev::f32_to_bf16(val);
                 }
         }

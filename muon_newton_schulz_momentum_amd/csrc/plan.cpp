@@ -32,6 +32,17 @@ void clear_error() { g_last_error.clear(); }
 
 namespace {
 
+// The update scale of a shape rule (MUON_SCALE_*), computed in float64 and rounded once
+// to float32.
+float rule_scale(int32_t mode, int64_t rows, int64_t cols) {
+    const double r = (double)rows, c = (double)cols;
+    switch (mode) {
+        case MUON_SCALE_ASPECT: return (float)std::sqrt(r / c > 1.0 ? r / c : 1.0);
+        case MUON_SCALE_RMS_MATCH: return (float)(0.2 * std::sqrt(r > c ? r : c));
+        default: return 1.0f;
+    }
+}
+
 int32_t pick_tile(int64_t m) {
     if (m >= 1024) return TILE_256;
     if (m > 128) return TILE_128;
@@ -100,6 +111,9 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (n > 0 && !params) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: params is NULL");
     const uint64_t cap = opts ? opts->max_workspace_bytes : 0;
     const float* scales = opts ? opts->scale : nullptr;
+    const int32_t scale_mode = opts ? opts->scale_mode : MUON_SCALE_NONE;
+    if (scale_mode != MUON_SCALE_NONE && scale_mode != MUON_SCALE_ASPECT && scale_mode != MUON_SCALE_RMS_MATCH)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown scale_mode");
     const uint32_t flags = opts ? opts->flags : 0u;
 
     // ---- validate every descriptor -----------------------------------------------------
@@ -229,7 +243,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
                 r.chunk = cidx; r.slot = s;
                 MatEntry e{};
                 e.w = r.w; e.m = r.m; e.g = r.g; e.rows = r.rows; e.cols = r.cols;
-                e.trans = r.trans; e.scale = scales ? scales[pi] : 1.0f;
+                e.trans = r.trans; e.scale = scales ? scales[pi] : rule_scale(scale_mode, r.rows, r.cols);
                 p->table.push_back(e);
             }
             start += cnt;
@@ -306,6 +320,7 @@ muon_status muon_plan_param_info(const muon_plan* plan, int64_t param, muon_para
     out->chunk = r.chunk;
     out->slot = r.slot;
     out->transposed = r.trans;
+    out->scale = plan->table[(size_t)(c.first + r.slot)].scale;
     out->output_offset = c.off_xp + (uint64_t)r.slot * c.mp * c.np * 2ull;
     out->ld = c.np;
     return MUON_OK;

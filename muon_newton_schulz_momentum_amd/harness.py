@@ -58,7 +58,8 @@ class Plan:
     """One bound libmuon plan over a list of parameters."""
 
     def __init__(self, params: Sequence[ParamTensors], max_workspace_bytes: int = 0,
-                 scales: Optional[Sequence[float]] = None, device=None, bind: bool = True, flags: int = 0):
+                 scales: Optional[Sequence[float]] = None, device=None, bind: bool = True, flags: int = 0,
+                 scale_mode: int = 0):
         self.params = list(params)
         n = len(self.params)
         self._descs = (L.muon_param_desc * max(n, 1))()
@@ -67,6 +68,7 @@ class Plan:
         opts = L.muon_plan_opts()
         opts.max_workspace_bytes = int(max_workspace_bytes)
         opts.flags = int(flags)
+        opts.scale_mode = int(scale_mode)
         self._scales = None
         if scales is not None:
             self._scales = (C.c_float * max(n, 1))(*[float(s) for s in scales])
@@ -122,6 +124,45 @@ class Plan:
              chunk: int = -1, stream=None):
         L.check(L.muon_step(self._plan, chunk, beta, a, b, c, steps, eps, lr, wd, _stream_ptr(stream)),
                 "muon_step")
+
+    def ns_schedule(self, coeffs, eps=wl.NS_EPS, chunk: int = -1, stream=None):
+        """Newton–Schulz with per-iteration coefficients: coeffs is a (steps, 3) sequence."""
+        flat = [float(v) for row in coeffs for v in row]
+        arr = (C.c_float * len(flat))(*flat)
+        L.check(L.muon_ns_batched_schedule(self._plan, chunk, arr, len(flat) // 3, eps, _stream_ptr(stream)),
+                "muon_ns_batched_schedule")
+
+    @staticmethod
+    def config(beta, lr, wd, a=wl.NS_A, b=wl.NS_B, c=wl.NS_C, steps=wl.NS_STEPS, eps=wl.NS_EPS,
+               coeffs=None, nesterov=False, dev_scalars: Optional[torch.Tensor] = None):
+        """A muon_step_config (and the host arrays it points to, which must stay alive)."""
+        k = L.muon_step_config()
+        k.beta, k.lr, k.wd, k.eps = beta, lr, wd, eps
+        k.a, k.b, k.c = a, b, c
+        keep = None
+        if coeffs is not None:
+            flat = [float(v) for row in coeffs for v in row]
+            keep = (C.c_float * len(flat))(*flat)
+            k.coeffs = keep
+            steps = len(flat) // 3
+        k.steps = steps
+        k.nesterov = 1 if nesterov else 0
+        if dev_scalars is not None:
+            assert dev_scalars.dtype == torch.float32 and dev_scalars.numel() >= 3 and dev_scalars.is_cuda
+            k.dev_scalars = dev_scalars.data_ptr()
+        return k, keep
+
+    def step_ex(self, beta, lr, wd, chunk: int = -1, stream=None, **kw):
+        k, keep = self.config(beta, lr, wd, **kw)
+        L.check(L.muon_step_ex(self._plan, chunk, C.byref(k), _stream_ptr(stream)), "muon_step_ex")
+        del keep
+
+    def capture_ex(self, beta, lr, wd, **kw) -> "Graph":
+        k, keep = self.config(beta, lr, wd, **kw)
+        g = C.c_void_p()
+        L.check(L.muon_graph_capture_ex(self._plan, C.byref(k), C.byref(g)), "muon_graph_capture_ex")
+        del keep
+        return Graph(g, self)
 
     def capture(self, beta, lr, wd, a=wl.NS_A, b=wl.NS_B, c=wl.NS_C, steps=wl.NS_STEPS,
                 eps=wl.NS_EPS) -> "Graph":

@@ -41,8 +41,11 @@ __all__ = [
     "ns_iteration_rows",
     "frobenius_normalise",
     "ns_iterate",
+    "ns_iterate_schedule",
+    "newton_schulz_schedule",
     "newton_schulz",
     "apply_update",
+    "update_scale",
     "muon_step_ref",
 ]
 
@@ -81,16 +84,21 @@ def bf16_round(x) -> np.ndarray:
     return out
 
 
-def momentum_update(M, G, beta):
+def momentum_update(M, G, beta, nesterov=False):
     """Momentum EMA in float64 with one float32 store; returns (M_new as float32, X0 bf16-valued).
 
     READING (the pages only say the FP32 momentum shard is updated locally and then cast
     to BF16 — notes page section 5 step 1; recipe page, "How to Make Parameter Updates
-    Faster and More Stable?"): M <- beta*M + (1-beta)*G, no Nesterov term.
+    Faster and More Stable?"): M <- beta*M + (1-beta)*G, and by default no Nesterov term.
 
     (1-beta) is formed in float32 as the library forms it.  Both products are exact in
     float64 (24-bit by 24-bit significands); the sum is rounded once to float64 and then
     once to float32.  G may hold float32 or bfloat16 values; both widen exactly.
+
+    With nesterov=True the matrix handed on is the look-ahead N = beta*M_new + (1-beta)*G,
+    formed the same way (float64 products and sum, one float32 rounding) and then cast;
+    the returned momentum is M_new either way.  READING: the pages orthogonalise the
+    momentum itself; the look-ahead is the common Muon variant, offered as an option.
     """
     b32 = np.float32(beta)
     omb32 = np.float32(1.0) - b32
@@ -98,6 +106,9 @@ def momentum_update(M, G, beta):
     G64 = np.asarray(G, dtype=np.float64)
     acc = np.float64(b32) * M64 + np.float64(omb32) * G64
     M_new = acc.astype(np.float32)
+    if nesterov:
+        N = (np.float64(b32) * M_new.astype(np.float64) + np.float64(omb32) * G64).astype(np.float32)
+        return M_new, bf16_round(N.astype(np.float64))
     X0 = bf16_round(M_new.astype(np.float64))
     return M_new, X0
 
@@ -148,6 +159,37 @@ def ns_iterate(X, a, b, c, steps, emulate_bf16=True):
         B = R(b * A + c * (A @ A))
         X = R(a * X + B @ X)
     return X
+
+
+def ns_iterate_schedule(X, coeffs, emulate_bf16=True):
+    """Newton–Schulz steps with their own coefficients: coeffs = [(a_1, b_1, c_1), ...].
+
+    Step t is the step of ns_iterate with (a_t, b_t, c_t), so every singular value s maps
+    through p_t(s) = a_t s + b_t s^3 + c_t s^5 in turn.  READING: the pages fix no
+    coefficients; a per-step schedule is offered next to the constant one.
+    """
+    R = bf16_round if emulate_bf16 else (lambda v: v)
+    X = np.asarray(X, dtype=np.float64)
+    for a, b, c in coeffs:
+        a = f32(a)[()]
+        b = f32(b)[()]
+        c = f32(c)[()]
+        A = R(X @ X.T)
+        B = R(b * A + c * (A @ A))
+        X = R(a * X + B @ X)
+    return X
+
+
+def newton_schulz_schedule(X0, coeffs, eps, emulate_bf16=True):
+    """newton_schulz with a per-step coefficient schedule (orientation, normalisation, steps)."""
+    X0 = np.asarray(X0, dtype=np.float64)
+    if X0.ndim != 2:
+        raise ValueError("Newton–Schulz takes 2-D matrices only")
+    t = canonical_orientation(*X0.shape)
+    Xc = X0.T if t else X0
+    X = frobenius_normalise(Xc, eps, emulate_bf16)
+    O = ns_iterate_schedule(X, coeffs, emulate_bf16)
+    return O.T if t else O
 
 
 def ns_iteration_rows(X, a, b, c, rows, emulate_bf16=True):
@@ -207,6 +249,28 @@ def apply_update(W, O, lr, wd, scale=1.0):
     t1 = d * W64
     t2 = u * O64
     return (t1 - t2).astype(np.float32)
+
+
+def update_scale(rule, rows, cols):
+    """The update scale s_i of a shape rule, as the float32 value the library uses.
+
+    READING (the pages give no rule; one notes that careful per-parameter update scaling
+    mattered in the prior work it names, Russian page, section on Muon versus AdamW):
+      "none"       s = 1
+      "aspect"     s = sqrt(max(1, rows / cols))   (rows = outputs of the stored matrix)
+      "rms_match"  s = 0.2 * sqrt(max(rows, cols)) (an update RMS near AdamW's)
+    Each is evaluated in float64 and rounded once to float32.
+    """
+    r, c = float(rows), float(cols)
+    if rule == "none":
+        v = 1.0
+    elif rule == "aspect":
+        v = np.sqrt(max(1.0, r / c))
+    elif rule == "rms_match":
+        v = 0.2 * np.sqrt(max(r, c))
+    else:
+        raise ValueError(f"unknown update-scale rule {rule!r}")
+    return float(np.float32(v))
 
 
 def muon_step_ref(W, M, G, *, beta, a, b, c, steps, eps, lr, wd, scale=1.0,

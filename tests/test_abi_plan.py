@@ -285,3 +285,34 @@ def test_fused_small_path_is_chosen_by_shape_and_flag():
         assert got == expect
         L.muon_plan_destroy(p)
     assert L.muon_kernel_name(L.MUON_KERNEL_NS_SMALL) == b"ns_small"
+
+
+def test_scale_modes_set_each_parameters_update_scale():
+    from oracle import muon_oracle as orc
+    shapes = [(4096, 1024), (1024, 4096), (2048, 2048), (5632, 2048), (300,)]
+    for mode, rule in ((L.MUON_SCALE_NONE, "none"), (L.MUON_SCALE_ASPECT, "aspect"),
+                       (L.MUON_SCALE_RMS_MATCH, "rms_match")):
+        opts = L.muon_plan_opts()
+        opts.scale_mode = mode
+        p = C.c_void_p()
+        assert L.muon_plan_buckets(_descs(shapes), len(shapes), C.byref(opts), C.byref(p)) == 0
+        for i, shp in enumerate(shapes):
+            info = L.muon_param_info()
+            L.check(L.muon_plan_param_info(p, i, C.byref(info)), "param_info")
+            if len(shp) == 2:
+                assert info.scale == orc.update_scale(rule, *shp), (rule, shp)
+        L.muon_plan_destroy(p)
+    # an explicit scale array wins over the rule; an unknown rule is refused
+    opts = L.muon_plan_opts()
+    opts.scale_mode = L.MUON_SCALE_ASPECT
+    keep = (C.c_float * 1)(0.5)
+    opts.scale = keep
+    p = C.c_void_p()
+    assert L.muon_plan_buckets(_descs([(4096, 1024)]), 1, C.byref(opts), C.byref(p)) == 0
+    info = L.muon_param_info()
+    L.check(L.muon_plan_param_info(p, 0, C.byref(info)), "param_info")
+    assert info.scale == 0.5
+    L.muon_plan_destroy(p)
+    opts = L.muon_plan_opts()
+    opts.scale_mode = 7
+    assert L.muon_plan_buckets(_descs([(64, 64)]), 1, C.byref(opts), C.byref(p)) == L.MUON_ERR_INVALID_ARG

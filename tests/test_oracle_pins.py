@@ -476,3 +476,92 @@ def test_step_cast_points_and_order():
     np.testing.assert_array_equal(out["O"], orc.bf16_round(out["O"]))
     np.testing.assert_array_equal(out["W"], orc.apply_update(W, out["O"], 0.02, 0.1))
     assert out["W"].dtype == np.float32 and out["M"].dtype == np.float32
+
+
+# ----------------------------------------------------------------------------------------
+# update-scale rules
+# ----------------------------------------------------------------------------------------
+
+def test_update_scale_rules_exact_values():
+    # values the formulas fix exactly (perfect squares, and 1 for wide matrices)
+    assert orc.update_scale("none", 4096, 1024) == 1.0
+    assert orc.update_scale("aspect", 4096, 1024) == 2.0          # sqrt(4)
+    assert orc.update_scale("aspect", 9 * 64, 64) == 3.0          # sqrt(9)
+    assert orc.update_scale("aspect", 1024, 4096) == 1.0          # wide: max(1, 1/4)
+    assert orc.update_scale("aspect", 2048, 2048) == 1.0
+    assert orc.update_scale("rms_match", 1024, 4096) == float(np.float32(0.2 * 64.0))
+    assert orc.update_scale("rms_match", 4096, 1024) == float(np.float32(0.2 * 64.0))   # symmetric
+    assert orc.update_scale("rms_match", 100, 2500) == float(np.float32(0.2 * 50.0))
+    # aspect never shrinks an update; rms_match grows as the square root of the long side
+    for r, c in ((5632, 2048), (32, 4096), (8704, 3072)):
+        assert orc.update_scale("aspect", r, c) >= 1.0
+        assert abs(orc.update_scale("rms_match", r, c) / orc.update_scale("rms_match", 4 * r, 4 * c) - 0.5) < 1e-7
+    with pytest.raises(ValueError):
+        orc.update_scale("bogus", 2, 2)
+
+
+# ----------------------------------------------------------------------------------------
+# coefficient schedules and the Nesterov look-ahead
+# ----------------------------------------------------------------------------------------
+
+SCHEDULE = [(4.0848, -6.8946, 2.9270), (3.9505, -6.3029, 2.6377), (3.7418, -5.5913, 2.3037),
+            (2.8769, -3.1427, 1.2046), (2.8366, -3.0525, 1.2012)]
+
+
+def test_schedule_exact_mode_is_composed_svd_polynomial():
+    rng = np.random.default_rng(31)
+    X0 = rng.standard_normal((24, 40))
+    U, S, Vt = np.linalg.svd(X0, full_matrices=False)
+    s = S / (np.linalg.norm(X0) + float(np.float32(EPS)))
+    for a, b, c in SCHEDULE:
+        a, b, c = (float(np.float32(v)) for v in (a, b, c))
+        s = a * s + b * s ** 3 + c * s ** 5
+    want = (U * s) @ Vt
+    got = orc.newton_schulz_schedule(X0, SCHEDULE, EPS, emulate_bf16=False)
+    assert np.linalg.norm(got - want) / np.linalg.norm(want) < 1e-10
+    # the transpose goes through the canonical orientation
+    got_t = orc.newton_schulz_schedule(X0.T, SCHEDULE, EPS, emulate_bf16=False)
+    assert np.linalg.norm(got_t - want.T) / np.linalg.norm(want) < 1e-10
+
+
+def test_schedule_bf16_bruteforce_rational():
+    rng = np.random.default_rng(32)
+    X = orc.bf16_round(rng.integers(-40, 41, (3, 5)).astype(np.float64) / 64.0)
+    sched = SCHEDULE[:2]
+    Xr = _frac_mat(X)
+    for a, b, c in sched:
+        a, b, c = (Fraction(float(np.float32(v))) for v in (a, b, c))
+        Ar = _rb(_mm(Xr, [list(r) for r in zip(*Xr)]))
+        AA = _mm(Ar, Ar)
+        Br = _rb([[b * Ar[i][j] + c * AA[i][j] for j in range(3)] for i in range(3)])
+        BX = _mm(Br, Xr)
+        Xr = _rb([[a * Xr[i][j] + BX[i][j] for j in range(5)] for i in range(3)])
+    got = orc.ns_iterate_schedule(X, sched, emulate_bf16=True)
+    np.testing.assert_array_equal(got, np.array([[float(v) for v in row] for row in Xr]))
+
+
+def test_nesterov_lookahead_closed_form_and_rational():
+    # constant G from M0 = 0: M_t = (1 - beta^t) G, look-ahead N_t = (1 - beta^(t+1)) G
+    beta = 0.9
+    G = np.random.default_rng(33).standard_normal(64).astype(np.float32)
+    M = np.zeros_like(G)
+    b = float(np.float32(beta))
+    for t in range(1, 8):
+        M, X0 = orc.momentum_update(M, G, beta, nesterov=True)
+        want = (1.0 - b ** (t + 1)) * G.astype(np.float64)
+        np.testing.assert_allclose(X0, want, rtol=2 ** -8 + t * 2 ** -23, atol=0)
+    # one step by exact rationals: N = RN32(RN64(b*M_new + (1-b)*G)), X0 = RNE_bf16(N)
+    rng = np.random.default_rng(34)
+    M0 = rng.standard_normal(40).astype(np.float32)
+    G0 = rng.standard_normal(40).astype(np.float32)
+    M1, X1 = orc.momentum_update(M0, G0, 0.95, nesterov=True)
+    b = Fraction(float(np.float32(0.95)))
+    omb = Fraction(float(np.float32(1.0) - np.float32(0.95)))
+    for m0, g0, m1, x1 in zip(M0, G0, M1, X1):
+        m_new = Fraction(float(np.float32(float(b * Fraction(float(m0)) + omb * Fraction(float(g0))))))
+        assert float(m_new) == float(m1)
+        n64 = float(b * m_new + omb * Fraction(float(g0)))          # one float64 rounding
+        assert x1 == _nearest_bf16_bruteforce(float(np.float32(n64)))
+    # beta = 0: the look-ahead is G itself (rounded to bf16)
+    _, X = orc.momentum_update(M0, G0, 0.0, nesterov=True)
+    np.testing.assert_array_equal(X, orc.bf16_round(G0.astype(np.float64)))
