@@ -62,13 +62,21 @@ typedef int32_t muon_status;
 #define MUON_DTYPE_F32 0
 #define MUON_DTYPE_BF16 1
 
-/* One parameter as the caller holds it.  Only ndim == 2 parameters take the Muon step
- * (the pages apply Muon to every 2-D non-embedding matrix and AdamW to the rest —
- * "Frontier Pre-training at Microsoft AI", setup section 4); any other ndim is counted
- * as excluded and its pointers are not read.
- * weight, momentum: device, rows x cols float32, row-major, contiguous, 16-B aligned.
- * grad: device, rows x cols of grad_dtype, row-major, contiguous, 16-B aligned.
- * weight and momentum must not overlap each other, any other parameter's, or a grad. */
+/* One parameter as the caller holds it.  The pages apply Muon to every 2-D matrix that is
+ * not an embedding and AdamW to the rest, scalars and embeddings ("Frontier Pre-training
+ * at Microsoft AI", setup section 4; "Microsoft Reveals MAI-Base-2 Training Recipe ...",
+ * section "How to Make Parameter Updates Faster and More Stable?").  `optimizer` says
+ * which one a parameter takes:
+ *   MUON_OPT_DEFAULT  ndim == 2: Muon; otherwise AdamW when exp_avg_sq is non-NULL,
+ *                     else excluded (its pointers are then not read);
+ *   MUON_OPT_ADAMW    AdamW whatever ndim (embeddings);
+ *   MUON_OPT_NONE     excluded.
+ * Muon: weight, momentum are rows x cols float32, grad rows x cols of grad_dtype, all
+ * row-major, contiguous, device, 16-B aligned.  AdamW: weight, momentum (the first
+ * moment), exp_avg_sq (the second moment) are float32 and grad of grad_dtype, each
+ * rows * cols contiguous elements (a parameter of another ndim passes rows = its
+ * element count and cols = 1), device, 16-B aligned.  Written buffers (weight,
+ * momentum, exp_avg_sq) must not overlap each other, any other parameter's, or a grad. */
 typedef struct muon_param_desc {
     int32_t ndim;
     int32_t grad_dtype; /* MUON_DTYPE_F32 or MUON_DTYPE_BF16 */
@@ -77,7 +85,14 @@ typedef struct muon_param_desc {
     float* weight;
     float* momentum;
     const void* grad;
+    float* exp_avg_sq;  /* AdamW only */
+    int32_t optimizer;  /* MUON_OPT_* */
+    int32_t reserved;
 } muon_param_desc;
+
+#define MUON_OPT_DEFAULT 0
+#define MUON_OPT_ADAMW 1
+#define MUON_OPT_NONE 2
 
 /* Plan options.  A zero-filled struct (or NULL) means: no workspace cap, scale 1. */
 typedef struct muon_plan_opts {
@@ -136,7 +151,7 @@ typedef struct muon_chunk_info {
 
 /* Where one parameter's orthogonalised update O lives after muon_ns_batched. */
 typedef struct muon_param_info {
-    int32_t included;       /* 0 for excluded (ndim != 2) parameters; rest is then 0  */
+    int32_t included;       /* 1: Muon; 2: AdamW; 0: excluded (for 0 and 2 the rest is 0) */
     int32_t chunk;
     int64_t slot;           /* index of the matrix inside its chunk                   */
     int32_t transposed;     /* 1 when rows > cols: O is stored as the m x n transpose */
@@ -161,9 +176,12 @@ MUON_API muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
 /* Bytes of device workspace the plan needs (256-B aligned start required). */
 MUON_API muon_status muon_plan_workspace_bytes(const muon_plan* plan, uint64_t* bytes);
 
-/* Number of chunks; counts of included and excluded parameters (any pointer may be NULL). */
+/* Number of chunks and buckets; counts of the parameters that take Muon (included) and
+ * of those that take neither optimizer (excluded).  Any pointer may be NULL. */
 MUON_API muon_status muon_plan_counts(const muon_plan* plan, int32_t* n_chunks, int32_t* n_buckets,
                              int64_t* n_included, int64_t* n_excluded);
+/* Count and total elements of the parameters that take AdamW (any pointer may be NULL). */
+MUON_API muon_status muon_plan_adamw_counts(const muon_plan* plan, int64_t* n_params, int64_t* n_elements);
 
 MUON_API muon_status muon_plan_info(const muon_plan* plan, int32_t chunk, muon_chunk_info* out);
 
@@ -225,6 +243,28 @@ MUON_API muon_status muon_step(const muon_plan* plan, int32_t chunk, float beta,
 MUON_API muon_status muon_ns_batched_schedule(const muon_plan* plan, int32_t chunk, const float* coeffs,
                                      int32_t steps, float eps, void* stream);
 
+/* AdamW for the parameters that take it (the pages' companion optimizer, see
+ * muon_param_desc), decoupled weight decay as in the Muon apply.  Per element, float64
+ * arithmetic with every operation rounded once, in this order, then float32 stores:
+ *     m = beta1*m + (1-beta1)*g;   v = beta2*v + (1-beta2)*(g*g);
+ *     w = (1 - lr*wd)*w - (lr * (m / bc1)) / (sqrt(v / bc2) + eps),
+ * with bc1 = 1 - beta1^t, bc2 = 1 - beta2^t formed in float64 on the host (the float32 m
+ * and v are the values stored).  The pages give no AdamW hyper-parameters. */
+typedef struct muon_adamw_config {
+    float lr, beta1, beta2, eps, wd;
+    int32_t reserved;
+    int64_t step;              /* t >= 1, for the bias corrections                      */
+    /* Device, nullable, 4-byte aligned: {lr, wd, bc1, bc2} as four floats, read by the
+     * kernel when it runs instead of lr, wd and the bias corrections from `step` (for
+     * graph replays; bc1 and bc2 are then float32 values). */
+    const float* dev_scalars;
+} muon_adamw_config;
+
+/* AdamW over every AdamW parameter of the plan, one launch.  Errors: INVALID_ARG (NULL
+ * config, step < 1, non-finite or out-of-range hyper-parameters), ALIGNMENT, NOT_BOUND,
+ * HIP.  Nothing is launched when the plan has no AdamW parameter. */
+MUON_API muon_status muon_adamw_step(const muon_plan* plan, const muon_adamw_config* config, void* stream);
+
 /* Everything one step takes, for muon_step_ex and muon_graph_capture_ex. */
 typedef struct muon_step_config {
     float beta;                /* momentum coefficient                                     */
@@ -244,6 +284,9 @@ typedef struct muon_step_config {
      * the new values into this buffer, ordered before each launch.  Non-finite values
      * are not checked; they propagate as data. */
     const float* dev_scalars;
+    /* Host, nullable: also run AdamW over the plan's AdamW parameters (after the Muon
+     * step, on the same stream), so one call updates every parameter. */
+    const muon_adamw_config* adamw;
 } muon_step_config;
 
 /* muon_step with a muon_step_config.  Errors: INVALID_ARG (NULL config, chunk, steps,
@@ -293,7 +336,8 @@ MUON_API void muon_graph_destroy(muon_graph* graph);
 #define MUON_KERNEL_GEMM_AXPY 5
 #define MUON_KERNEL_APPLY 6
 #define MUON_KERNEL_NS_SMALL 7
-#define MUON_KERNEL_COUNT 8
+#define MUON_KERNEL_ADAMW 8
+#define MUON_KERNEL_COUNT 9
 
 /* Start recording a HIP event pair around every kernel launch of this plan (up to
  * `capacity` launches; later ones go unrecorded).  capacity = 0 stops recording.

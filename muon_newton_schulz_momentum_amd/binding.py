@@ -44,7 +44,12 @@ MUON_KERNEL_SYRK_POLY = 4
 MUON_KERNEL_GEMM_AXPY = 5
 MUON_KERNEL_APPLY = 6
 MUON_KERNEL_NS_SMALL = 7
-MUON_KERNEL_COUNT = 8
+MUON_KERNEL_ADAMW = 8
+MUON_KERNEL_COUNT = 9
+
+MUON_OPT_DEFAULT = 0
+MUON_OPT_ADAMW = 1
+MUON_OPT_NONE = 2
 
 MUON_PLAN_TILED_SMALL = 1
 
@@ -56,7 +61,13 @@ MUON_SCALE_RMS_MATCH = 2
 class muon_param_desc(C.Structure):
     _fields_ = [("ndim", C.c_int32), ("grad_dtype", C.c_int32), ("rows", C.c_int64),
                 ("cols", C.c_int64), ("weight", C.c_void_p), ("momentum", C.c_void_p),
-                ("grad", C.c_void_p)]
+                ("grad", C.c_void_p), ("exp_avg_sq", C.c_void_p), ("optimizer", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class muon_adamw_config(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("wd", C.c_float), ("reserved", C.c_int32), ("step", C.c_int64), ("dev_scalars", C.c_void_p)]
 
 
 class muon_plan_opts(C.Structure):
@@ -77,7 +88,8 @@ class muon_chunk_info(C.Structure):
 class muon_step_config(C.Structure):
     _fields_ = [("beta", C.c_float), ("lr", C.c_float), ("wd", C.c_float), ("eps", C.c_float),
                 ("steps", C.c_int32), ("a", C.c_float), ("b", C.c_float), ("c", C.c_float),
-                ("coeffs", C.POINTER(C.c_float)), ("nesterov", C.c_int32), ("dev_scalars", C.c_void_p)]
+                ("coeffs", C.POINTER(C.c_float)), ("nesterov", C.c_int32), ("dev_scalars", C.c_void_p),
+                ("adamw", C.POINTER(muon_adamw_config))]
 
 
 class muon_param_info(C.Structure):
@@ -112,6 +124,8 @@ muon_ns_batched = _fn("muon_ns_batched", C.c_int32,
 muon_apply = _fn("muon_apply", C.c_int32, [_P, C.c_int32, C.c_float, C.c_float, C.c_void_p])
 muon_ns_batched_schedule = _fn("muon_ns_batched_schedule", C.c_int32,
                                [_P, C.c_int32, C.POINTER(C.c_float), C.c_int32, C.c_float, C.c_void_p])
+muon_adamw_step = _fn("muon_adamw_step", C.c_int32, [_P, C.POINTER(muon_adamw_config), C.c_void_p])
+muon_plan_adamw_counts = _fn("muon_plan_adamw_counts", C.c_int32, [_P, C.POINTER(C.c_int64), C.POINTER(C.c_int64)])
 muon_step_ex = _fn("muon_step_ex", C.c_int32, [_P, C.c_int32, C.POINTER(muon_step_config), C.c_void_p])
 muon_step = _fn("muon_step", C.c_int32,
                 [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float,
@@ -136,7 +150,8 @@ muon_last_error = _fn("muon_last_error", C.c_char_p, [])
 EXPORTED = [
     "muon_plan_buckets", "muon_plan_workspace_bytes", "muon_plan_counts", "muon_plan_info",
     "muon_plan_param_info", "muon_plan_validate", "muon_plan_bind", "muon_momentum_update",
-    "muon_ns_batched", "muon_ns_batched_schedule", "muon_apply", "muon_step", "muon_step_ex",
+    "muon_ns_batched", "muon_ns_batched_schedule", "muon_apply", "muon_adamw_step", "muon_plan_adamw_counts",
+    "muon_step", "muon_step_ex",
     "muon_graph_capture", "muon_graph_capture_ex", "muon_graph_launch",
     "muon_graph_node_count", "muon_graph_destroy", "muon_timing_enable", "muon_timing_read",
     "muon_timing_reset", "muon_kernel_name", "muon_plan_destroy", "muon_status_string",

@@ -66,7 +66,47 @@ struct StepCfg {
     std::vector<float> abc;          // (a, b, c) of each iteration, 3 * steps values
     bool nesterov = false;
     const float* dev = nullptr;      // device {beta, lr, wd}, read by the kernels when set
+    bool adam = false;               // also run AdamW with `adam_args`
+    AdamArgs adam_args{};
 };
+
+// AdamW launch arguments from the public config (validated); tables filled in at launch.
+muon_status make_adam(const muon_adamw_config* c, AdamArgs& a, const char* who) {
+    if (!c) return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": AdamW config is NULL");
+    if (c->step < 1) return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": AdamW step must be >= 1");
+    if (!std::isfinite(c->lr) || !std::isfinite(c->wd) || !std::isfinite(c->eps) || c->eps < 0.f ||
+        !std::isfinite(c->beta1) || !std::isfinite(c->beta2) || c->beta1 < 0.f || c->beta1 >= 1.f ||
+        c->beta2 < 0.f || c->beta2 >= 1.f)
+        return set_error(MUON_ERR_INVALID_ARG,
+                         std::string(who) + ": AdamW lr, wd finite, eps >= 0, betas in [0, 1)");
+    if (c->dev_scalars && ((uintptr_t)c->dev_scalars & 3u) != 0)
+        return set_error(MUON_ERR_ALIGNMENT, std::string(who) + ": AdamW dev_scalars must be 4-byte aligned");
+    a.lr = (double)c->lr;
+    a.wd = (double)c->wd;
+    a.beta1 = (double)c->beta1;
+    a.omb1 = (double)(1.0f - c->beta1);
+    a.beta2 = (double)c->beta2;
+    a.omb2 = (double)(1.0f - c->beta2);
+    a.eps = (double)c->eps;
+    // bias corrections 1 - beta^t in float64 (pow of the float32 beta, widened)
+    a.bc1 = 1.0 - std::pow((double)c->beta1, (double)c->step);
+    a.bc2 = 1.0 - std::pow((double)c->beta2, (double)c->step);
+    a.dev_scalars = c->dev_scalars;
+    return MUON_OK;
+}
+
+muon_status adam_run(const muon_plan* p, AdamArgs a, hipStream_t s) {
+    if (p->adam_segs.empty()) return MUON_OK;
+    a.entries = at<const AdamEntry>(p, p->off_adam);
+    a.segs = at<const AdamSeg>(p, p->off_adam_segs);
+    a.n_segs = (int64_t)p->adam_segs.size();
+    double work = 0.0;
+    for (const AdamEntry& e : p->adam) work += (double)e.numel * (e.grad_dtype == MUON_DTYPE_F32 ? 28.0 : 26.0);
+    TimedLaunch tl(p, MUON_KERNEL_ADAMW, work, s);
+    const hipError_t e = launch_adamw(a, s);
+    tl.done(s);
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "AdamW kernel launch");
+}
 
 void fill_abc(StepCfg& cfg, float a, float b, float c) {
     cfg.abc.resize(3 * (size_t)cfg.steps);
@@ -292,7 +332,7 @@ muon_status step_chunks(const muon_plan* p, int32_t chunk, const StepCfg& cfg, h
         if ((st = ns_all(p, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
         for (int32_t i = 0; i < nc; ++i)
             if ((st = apply_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
-        return MUON_OK;
+        return cfg.adam ? adam_run(p, cfg.adam_args, s) : MUON_OK;
     }
     for (int32_t i = 0; i < nc; ++i) {
         if (chunk != -1 && i != chunk) continue;
@@ -301,7 +341,8 @@ muon_status step_chunks(const muon_plan* p, int32_t chunk, const StepCfg& cfg, h
         if ((st = ns_one(p, i, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
         if ((st = apply_chunk(p, ch, cfg, s)) != MUON_OK) return st;
     }
-    return MUON_OK;
+    // the AdamW parameters once, with the whole step (not with a single chunk)
+    return (cfg.adam && chunk == -1) ? adam_run(p, cfg.adam_args, s) : MUON_OK;
 }
 
 // A StepCfg from the public config (validated).
@@ -326,6 +367,10 @@ muon_status make_cfg(const muon_step_config* c, StepCfg& cfg, const char* who) {
     cfg.eps = c->eps;
     cfg.nesterov = c->nesterov == 1;
     cfg.dev = c->dev_scalars;
+    if (c->adamw) {
+        if ((st = make_adam(c->adamw, cfg.adam_args, who)) != MUON_OK) return st;
+        cfg.adam = true;
+    }
     return MUON_OK;
 }
 
@@ -368,8 +413,17 @@ muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream)
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemsetAsync(ws, 0, p->ws_bytes, s);
     if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipMemsetAsync");
-    if (!p->table.empty()) {
-        e = hipMemcpyAsync(ws, p->table.data(), p->table.size() * sizeof(MatEntry), hipMemcpyHostToDevice, s);
+    if (!p->adam.empty()) {
+        e = hipMemcpyAsync(static_cast<char*>(ws) + p->off_adam, p->adam.data(), p->adam.size() * sizeof(AdamEntry),
+                           hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(static_cast<char*>(ws) + p->off_adam_segs, p->adam_segs.data(),
+                               p->adam_segs.size() * sizeof(AdamSeg), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: AdamW table upload");
+    }
+    if (!p->table.empty() || !p->adam.empty()) {
+        if (!p->table.empty())
+            e = hipMemcpyAsync(ws, p->table.data(), p->table.size() * sizeof(MatEntry), hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: table upload");
         // the host table is pageable memory owned by the plan; make sure the copy has
         // consumed it before the caller can free or change anything
@@ -453,6 +507,16 @@ muon_status muon_step_ex(const muon_plan* p, int32_t chunk, const muon_step_conf
     muon_status st = make_cfg(config, cfg, "muon_step_ex");
     if (st != MUON_OK) return st;
     return step_chunks(p, chunk, cfg, static_cast<hipStream_t>(stream));
+}
+
+muon_status muon_adamw_step(const muon_plan* p, const muon_adamw_config* config, void* stream) {
+    clear_error();
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_adamw_step: plan is NULL");
+    if (!p->bound) return set_error(MUON_ERR_NOT_BOUND, "muon_adamw_step: call muon_plan_bind first");
+    AdamArgs a{};
+    muon_status st = make_adam(config, a, "muon_adamw_step");
+    if (st != MUON_OK) return st;
+    return adam_run(p, a, static_cast<hipStream_t>(stream));
 }
 
 muon_status muon_step(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,
@@ -604,6 +668,7 @@ const char* muon_kernel_name(int32_t k) {
         case MUON_KERNEL_GEMM_AXPY: return "gemm_axpy";
         case MUON_KERNEL_APPLY: return "apply";
         case MUON_KERNEL_NS_SMALL: return "ns_small";
+        case MUON_KERNEL_ADAMW: return "adamw";
         default: return "unknown";
     }
 }

@@ -455,6 +455,79 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// AdamW for the parameters that take it.  Each operation is one float64 rounding, in the
+// order below (contraction is off in this file); m and v are stored as float32.
+// ---------------------------------------------------------------------------------------
+struct AdamHyper {
+    double lr, d, beta1, omb1, beta2, omb2, eps, bc1, bc2;
+};
+
+__device__ __forceinline__ void adam_elem(float& w, float& m, float& v, float g32, const AdamHyper& h) {
+    const double g = (double)g32;
+    m = (float)(h.beta1 * (double)m + h.omb1 * g);          // both products exact
+    v = (float)(h.beta2 * (double)v + h.omb2 * (g * g));    // g*g exact, omb2*g^2 rounded
+    const double mhat = (double)m / h.bc1;
+    const double vhat = (double)v / h.bc2;
+    const double den = sqrt(vhat) + h.eps;
+    const double upd = (h.lr * mhat) / den;
+    w = (float)(h.d * (double)w - upd);
+}
+
+__global__ __launch_bounds__(256) void adamw_kernel(AdamArgs a) {
+    AdamHyper h;
+    h.lr = a.lr;
+    double wd = a.wd;
+    h.bc1 = a.bc1;
+    h.bc2 = a.bc2;
+    if (a.dev_scalars) {
+        h.lr = (double)a.dev_scalars[0];
+        wd = (double)a.dev_scalars[1];
+        h.bc1 = (double)a.dev_scalars[2];
+        h.bc2 = (double)a.dev_scalars[3];
+    }
+    h.d = 1.0 - h.lr * wd;
+    h.beta1 = a.beta1; h.omb1 = a.omb1; h.beta2 = a.beta2; h.omb2 = a.omb2; h.eps = a.eps;
+    const int tid = threadIdx.x;
+    for (int64_t sg = blockIdx.x; sg < a.n_segs; sg += gridDim.x) {
+        const AdamSeg seg = a.segs[sg];
+        const AdamEntry e = a.entries[seg.entry];
+        // 4096 elements: lane l of a wave handles 16 bytes at 1 KB steps
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t idx = seg.start + k * 1024 + tid * 4;
+            if (idx >= e.numel) continue;
+            if (idx + 4 <= e.numel) {
+                float4 w = *reinterpret_cast<const float4*>(e.w + idx);
+                float4 m = *reinterpret_cast<const float4*>(e.m + idx);
+                float4 v = *reinterpret_cast<const float4*>(e.v + idx);
+                float g[4];
+                if (e.grad_dtype == MUON_DTYPE_F32) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(static_cast<const float*>(e.g) + idx);
+                    g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
+                } else {
+                    const uint2 g2 = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(e.g) + idx);
+                    g[0] = bf16_to_f32(g2.x & 0xffffu); g[1] = bf16_to_f32(g2.x >> 16);
+                    g[2] = bf16_to_f32(g2.y & 0xffffu); g[3] = bf16_to_f32(g2.y >> 16);
+                }
+                adam_elem(w.x, m.x, v.x, g[0], h);
+                adam_elem(w.y, m.y, v.y, g[1], h);
+                adam_elem(w.z, m.z, v.z, g[2], h);
+                adam_elem(w.w, m.w, v.w, g[3], h);
+                *reinterpret_cast<float4*>(e.w + idx) = w;
+                *reinterpret_cast<float4*>(e.m + idx) = m;
+                *reinterpret_cast<float4*>(e.v + idx) = v;
+            } else {
+                for (int64_t j = idx; j < e.numel; ++j) {
+                    const float g = e.grad_dtype == MUON_DTYPE_F32 ? static_cast<const float*>(e.g)[j]
+                                                                   : bf16_to_f32(static_cast<const uint16_t*>(e.g)[j]);
+                    adam_elem(e.w[j], e.m[j], e.v[j], g, h);
+                }
+            }
+        }
+    }
+}
+
 // Grid size for the grid-stride loops: enough blocks to fill 256 CUs many times over.
 inline unsigned grid_for(int64_t items, int64_t cap = 256 * 64) {
     return (unsigned)(items < cap ? (items > 0 ? items : 1) : cap);
@@ -479,6 +552,13 @@ hipError_t launch_finalize(const FinalizeArgs& a, int64_t count, hipStream_t s) 
 hipError_t launch_normalize(const NormalizeArgs& a, hipStream_t s) {
     const unsigned grid = grid_for((a.total_units + 256 * UPT - 1) / (256 * UPT), 256 * 16);
     hipLaunchKernelGGL(normalize_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamArgs& a, hipStream_t s) {
+    if (a.n_segs <= 0) return hipSuccess;
+    const unsigned grid = grid_for(a.n_segs);
+    hipLaunchKernelGGL(adamw_kernel, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

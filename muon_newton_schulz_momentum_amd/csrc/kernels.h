@@ -49,6 +49,14 @@ struct ApplyArgs {
     const float* dev_scalars;  // nullable device {beta, lr, wd}: lr and wd are read from it instead
 };
 
+struct AdamArgs {
+    const AdamEntry* entries;
+    const AdamSeg* segs;
+    int64_t n_segs;
+    double lr, wd, beta1, omb1, beta2, omb2, eps, bc1, bc2;   // float32 inputs, widened
+    const float* dev_scalars;   // nullable device {lr, wd, bc1, bc2}
+};
+
 // Newton–Schulz GEMM kernels.  opa/opb are matrix-0 bases; every matrix of the chunk
 // sits `stride_*` elements after the previous one.
 enum NsMode : int32_t { NS_SYRK = 0, NS_POLY = 1, NS_AXPY = 2 };
@@ -97,6 +105,7 @@ hipError_t launch_momentum(const MomentumArgs& a, int32_t grad_dtype, hipStream_
 hipError_t launch_finalize(const FinalizeArgs& a, int64_t count, hipStream_t s);
 hipError_t launch_normalize(const NormalizeArgs& a, hipStream_t s);
 hipError_t launch_apply(const ApplyArgs& a, hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, hipStream_t s);
 hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_small(const SmallNsArgs& a, int64_t total, hipStream_t s);
 

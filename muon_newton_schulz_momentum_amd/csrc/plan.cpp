@@ -34,6 +34,15 @@ namespace {
 
 // The update scale of a shape rule (MUON_SCALE_*), computed in float64 and rounded once
 // to float32.
+// Which optimizer a parameter takes (see muon_param_desc).
+constexpr int32_t ROLE_NONE = 0, ROLE_MUON = 1, ROLE_ADAMW = 2;
+int32_t param_role(const muon_param_desc& d) {
+    if (d.optimizer == MUON_OPT_ADAMW) return ROLE_ADAMW;
+    if (d.optimizer == MUON_OPT_NONE) return ROLE_NONE;
+    if (d.ndim == 2) return ROLE_MUON;
+    return d.exp_avg_sq ? ROLE_ADAMW : ROLE_NONE;
+}
+
 float rule_scale(int32_t mode, int64_t rows, int64_t cols) {
     const double r = (double)rows, c = (double)cols;
     switch (mode) {
@@ -120,8 +129,30 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     std::vector<Interval> ivs;
     for (int64_t i = 0; i < n; ++i) {
         const muon_param_desc& d = params[i];
-        if (d.ndim != 2) continue;
         const std::string who = "parameter " + std::to_string(i);
+        if (d.optimizer != MUON_OPT_DEFAULT && d.optimizer != MUON_OPT_ADAMW && d.optimizer != MUON_OPT_NONE)
+            return set_error(MUON_ERR_INVALID_ARG, who + ": unknown optimizer");
+        const int32_t role = param_role(d);
+        if (role == ROLE_ADAMW) {
+            if (d.rows <= 0 || d.cols <= 0)
+                return set_error(MUON_ERR_SHAPE, who + ": rows and cols must be positive");
+            if (d.rows > (int64_t(1) << 40) || d.cols > (int64_t(1) << 31) || d.rows * d.cols > (int64_t(1) << 40))
+                return set_error(MUON_ERR_SHAPE, who + ": more than 2^40 elements");
+            if (d.grad_dtype != MUON_DTYPE_F32 && d.grad_dtype != MUON_DTYPE_BF16)
+                return set_error(MUON_ERR_INVALID_ARG, who + ": grad_dtype must be F32 or BF16");
+            if (!d.weight || !d.momentum || !d.exp_avg_sq || !d.grad)
+                return set_error(MUON_ERR_INVALID_ARG, who + ": weight, momentum, exp_avg_sq and grad must be non-NULL");
+            if (!aligned16(d.weight) || !aligned16(d.momentum) || !aligned16(d.exp_avg_sq) || !aligned16(d.grad))
+                return set_error(MUON_ERR_ALIGNMENT, who + ": buffers must be 16-byte aligned");
+            const uint64_t elems = (uint64_t)d.rows * (uint64_t)d.cols;
+            const uint64_t gsz = d.grad_dtype == MUON_DTYPE_F32 ? 4 : 2;
+            ivs.push_back({(uintptr_t)d.weight, (uintptr_t)d.weight + elems * 4, i, 0});
+            ivs.push_back({(uintptr_t)d.momentum, (uintptr_t)d.momentum + elems * 4, i, 1});
+            ivs.push_back({(uintptr_t)d.exp_avg_sq, (uintptr_t)d.exp_avg_sq + elems * 4, i, 1});
+            ivs.push_back({(uintptr_t)d.grad, (uintptr_t)d.grad + elems * gsz, i, 2});
+            continue;
+        }
+        if (role != ROLE_MUON) continue;
         if (d.rows <= 0 || d.cols <= 0)
             return set_error(MUON_ERR_SHAPE, who + ": rows and cols must be positive");
         if (d.rows > (int64_t(1) << 31) || d.cols > (int64_t(1) << 31))
@@ -166,14 +197,32 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: out of host memory");
     p->params.resize((size_t)n);
 
+    // ---- AdamW parameters: entries and fixed-size segments --------------------------------
+    for (int64_t i = 0; i < n; ++i) {
+        const muon_param_desc& d = params[i];
+        if (param_role(d) != ROLE_ADAMW) continue;
+        ParamRec& r = p->params[(size_t)i];
+        r.ndim = d.ndim; r.grad_dtype = d.grad_dtype; r.rows = d.rows; r.cols = d.cols;
+        r.w = d.weight; r.m = d.momentum; r.g = d.grad; r.v = d.exp_avg_sq;
+        r.included = ROLE_ADAMW; r.chunk = (int32_t)p->adam.size(); r.slot = -1; r.trans = 0;
+        AdamEntry e{};
+        e.w = d.weight; e.m = d.momentum; e.v = d.exp_avg_sq; e.g = d.grad;
+        e.numel = d.rows * d.cols; e.grad_dtype = d.grad_dtype;
+        for (int64_t s0 = 0; s0 < e.numel; s0 += ADAM_SEG) p->adam_segs.push_back(AdamSeg{r.chunk, 0, s0});
+        p->adam.push_back(e);
+        p->adam_elements += e.numel;
+    }
+
     // ---- bucket by canonical (m, n, grad dtype) ----------------------------------------
     std::map<std::tuple<int64_t, int64_t, int32_t>, std::vector<int64_t>> buckets;
     for (int64_t i = 0; i < n; ++i) {
         const muon_param_desc& d = params[i];
         ParamRec& r = p->params[(size_t)i];
+        const int32_t role = param_role(d);
+        if (role == ROLE_ADAMW) continue;
         r.ndim = d.ndim; r.grad_dtype = d.grad_dtype; r.rows = d.rows; r.cols = d.cols;
-        r.w = d.weight; r.m = d.momentum; r.g = d.grad;
-        r.included = d.ndim == 2; r.chunk = -1; r.slot = -1; r.trans = 0;
+        r.w = d.weight; r.m = d.momentum; r.g = d.grad; r.v = nullptr;
+        r.included = role == ROLE_MUON ? ROLE_MUON : 0; r.chunk = -1; r.slot = -1; r.trans = 0;
         if (!r.included) { p->n_excluded++; continue; }
         p->n_included++;
         r.trans = d.rows > d.cols;
@@ -201,7 +250,10 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
         geo.push_back(std::move(g));
     }
 
-    p->table_bytes = align_up((uint64_t)p->n_included * sizeof(MatEntry), WS_ALIGN);
+    // the start of the workspace: matrix table, AdamW entries, AdamW segments
+    p->off_adam = align_up((uint64_t)p->n_included * sizeof(MatEntry), WS_ALIGN);
+    p->off_adam_segs = p->off_adam + align_up((uint64_t)p->adam.size() * sizeof(AdamEntry), WS_ALIGN);
+    p->table_bytes = p->off_adam_segs + align_up((uint64_t)p->adam_segs.size() * sizeof(AdamSeg), WS_ALIGN);
     uint64_t total = p->table_bytes;
     for (const BucketGeo& g : geo)
         total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 6 * WS_ALIGN;
@@ -285,6 +337,13 @@ muon_status muon_plan_counts(const muon_plan* plan, int32_t* n_chunks, int32_t* 
     return MUON_OK;
 }
 
+muon_status muon_plan_adamw_counts(const muon_plan* plan, int64_t* n_params, int64_t* n_elements) {
+    if (!plan) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_adamw_counts: plan is NULL");
+    if (n_params) *n_params = (int64_t)plan->adam.size();
+    if (n_elements) *n_elements = plan->adam_elements;
+    return MUON_OK;
+}
+
 muon_status muon_plan_info(const muon_plan* plan, int32_t chunk, muon_chunk_info* out) {
     if (!plan || !out) return set_error(MUON_ERR_INVALID_ARG, "muon_plan_info: NULL argument");
     if (chunk < 0 || chunk >= (int32_t)plan->chunks.size())
@@ -315,6 +374,10 @@ muon_status muon_plan_param_info(const muon_plan* plan, int64_t param, muon_para
     std::memset(out, 0, sizeof(*out));
     const ParamRec& r = plan->params[(size_t)param];
     if (!r.included) return MUON_OK;
+    if (r.included == ROLE_ADAMW) {
+        out->included = ROLE_ADAMW;
+        return MUON_OK;
+    }
     const Chunk& c = plan->chunks[(size_t)r.chunk];
     out->included = 1;
     out->chunk = r.chunk;
@@ -333,10 +396,13 @@ muon_status muon_plan_validate(const muon_plan* plan, const muon_param_desc* par
     for (int64_t i = 0; i < n; ++i) {
         const muon_param_desc& d = params[i];
         const ParamRec& r = plan->params[(size_t)i];
+        const int32_t role = param_role(d);
+        if ((role == ROLE_NONE ? 0 : role) != r.included)
+            return set_error(MUON_ERR_STALE_PLAN, "parameter " + std::to_string(i) + ": optimizer changed");
+        if (role == ROLE_NONE) continue;
         if (d.ndim != r.ndim) return set_error(MUON_ERR_STALE_PLAN, "parameter " + std::to_string(i) + ": ndim changed");
-        if (d.ndim != 2) continue;
         if (d.rows != r.rows || d.cols != r.cols || d.grad_dtype != r.grad_dtype || d.weight != r.w ||
-            d.momentum != r.m || d.grad != r.g)
+            d.momentum != r.m || d.grad != r.g || (role == ROLE_ADAMW && d.exp_avg_sq != r.v))
             return set_error(MUON_ERR_STALE_PLAN, "parameter " + std::to_string(i) + ": shape, dtype or buffer changed");
     }
     return MUON_OK;

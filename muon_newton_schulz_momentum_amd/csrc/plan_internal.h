@@ -45,6 +45,23 @@ struct Chunk {
     uint64_t off_table;      // this chunk's first table row
 };
 
+// A parameter that takes AdamW (64 B), and one segment of ADAM_SEG of its elements.
+struct AdamEntry {
+    float* w;
+    float* m;
+    float* v;
+    const void* g;
+    int64_t numel;
+    int32_t grad_dtype;
+    int32_t pad[3];
+};
+struct AdamSeg {
+    int32_t entry;
+    int32_t pad;
+    int64_t start;
+};
+constexpr int64_t ADAM_SEG = 4096;   // elements per AdamW segment (one block's work)
+
 struct ParamRec {
     int32_t ndim;
     int32_t grad_dtype;
@@ -52,8 +69,9 @@ struct ParamRec {
     float* w;
     float* m;
     const void* g;
-    int32_t included;
-    int32_t chunk;
+    float* v = nullptr;      // AdamW second moment
+    int32_t included;        // 1 Muon, 2 AdamW, 0 excluded
+    int32_t chunk;           // Muon: chunk; AdamW: index in the AdamW table
     int64_t slot;
     int32_t trans;
 };
@@ -76,7 +94,11 @@ struct muon_plan {
     int64_t n_included = 0, n_excluded = 0;
     bool shared_regions = false;
     uint32_t flags = 0;      // MUON_PLAN_* bits
-    uint64_t table_bytes = 0;
+    uint64_t table_bytes = 0;    // matrix table + AdamW tables (the start of the workspace)
+    std::vector<muon::AdamEntry> adam;
+    std::vector<muon::AdamSeg> adam_segs;
+    int64_t adam_elements = 0;
+    uint64_t off_adam = 0, off_adam_segs = 0;
     uint64_t ws_bytes = 0;
     // bind state
     void* ws = nullptr;

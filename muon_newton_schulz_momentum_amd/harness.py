@@ -27,14 +27,22 @@ class ParamTensors:
     weight: torch.Tensor
     momentum: torch.Tensor
     grad: torch.Tensor
+    exp_avg_sq: Optional[torch.Tensor] = None   # AdamW second moment
+    optimizer: int = 0                          # MUON_OPT_*
 
 
 def _desc(p: ParamTensors) -> L.muon_param_desc:
     d = L.muon_param_desc()
     d.ndim = p.weight.dim()
-    if d.ndim != 2:
+    d.optimizer = int(p.optimizer)
+    adam = p.optimizer == L.MUON_OPT_ADAMW or (p.optimizer == L.MUON_OPT_DEFAULT and d.ndim != 2
+                                                and p.exp_avg_sq is not None)
+    if not adam and (d.ndim != 2 or p.optimizer == L.MUON_OPT_NONE):
         return d
-    for name, t in (("weight", p.weight), ("momentum", p.momentum), ("grad", p.grad)):
+    tensors = [("weight", p.weight), ("momentum", p.momentum), ("grad", p.grad)]
+    if adam:
+        tensors.append(("exp_avg_sq", p.exp_avg_sq))
+    for name, t in tensors:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
         if t.shape != p.weight.shape:
@@ -47,7 +55,13 @@ def _desc(p: ParamTensors) -> L.muon_param_desc:
         d.grad_dtype = L.MUON_DTYPE_BF16
     else:
         raise ValueError("grad must be float32 or bfloat16")
-    d.rows, d.cols = p.weight.shape
+    if adam:
+        if p.exp_avg_sq.dtype != torch.float32:
+            raise ValueError("exp_avg_sq must be float32")
+        d.rows, d.cols = p.weight.numel(), 1
+        d.exp_avg_sq = p.exp_avg_sq.data_ptr()
+    else:
+        d.rows, d.cols = p.weight.shape
     d.weight = p.weight.data_ptr()
     d.momentum = p.momentum.data_ptr()
     d.grad = p.grad.data_ptr()
@@ -134,7 +148,7 @@ class Plan:
 
     @staticmethod
     def config(beta, lr, wd, a=wl.NS_A, b=wl.NS_B, c=wl.NS_C, steps=wl.NS_STEPS, eps=wl.NS_EPS,
-               coeffs=None, nesterov=False, dev_scalars: Optional[torch.Tensor] = None):
+               coeffs=None, nesterov=False, dev_scalars: Optional[torch.Tensor] = None, adamw=None):
         """A muon_step_config (and the host arrays it points to, which must stay alive)."""
         k = L.muon_step_config()
         k.beta, k.lr, k.wd, k.eps = beta, lr, wd, eps
@@ -147,10 +161,31 @@ class Plan:
             steps = len(flat) // 3
         k.steps = steps
         k.nesterov = 1 if nesterov else 0
+        if adamw is not None:
+            keep = (keep, adamw)
+            k.adamw = C.pointer(adamw)
         if dev_scalars is not None:
             assert dev_scalars.dtype == torch.float32 and dev_scalars.numel() >= 3 and dev_scalars.is_cuda
             k.dev_scalars = dev_scalars.data_ptr()
         return k, keep
+
+    @staticmethod
+    def adamw_config(lr, beta1, beta2, eps, wd, step, dev_scalars: Optional[torch.Tensor] = None):
+        k = L.muon_adamw_config()
+        k.lr, k.beta1, k.beta2, k.eps, k.wd, k.step = lr, beta1, beta2, eps, wd, step
+        if dev_scalars is not None:
+            assert dev_scalars.dtype == torch.float32 and dev_scalars.numel() >= 4 and dev_scalars.is_cuda
+            k.dev_scalars = dev_scalars.data_ptr()
+        return k
+
+    def adamw_step(self, lr, beta1, beta2, eps, wd, step, stream=None, dev_scalars=None):
+        k = self.adamw_config(lr, beta1, beta2, eps, wd, step, dev_scalars)
+        L.check(L.muon_adamw_step(self._plan, C.byref(k), _stream_ptr(stream)), "muon_adamw_step")
+
+    def adamw_counts(self):
+        n, e = C.c_int64(), C.c_int64()
+        L.check(L.muon_plan_adamw_counts(self._plan, C.byref(n), C.byref(e)), "muon_plan_adamw_counts")
+        return int(n.value), int(e.value)
 
     def step_ex(self, beta, lr, wd, chunk: int = -1, stream=None, **kw):
         k, keep = self.config(beta, lr, wd, **kw)

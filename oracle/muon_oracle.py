@@ -46,6 +46,7 @@ __all__ = [
     "newton_schulz",
     "apply_update",
     "update_scale",
+    "adamw_update",
     "muon_step_ref",
 ]
 
@@ -271,6 +272,43 @@ def update_scale(rule, rows, cols):
     else:
         raise ValueError(f"unknown update-scale rule {rule!r}")
     return float(np.float32(v))
+
+
+def adamw_update(W, M, V, G, *, lr, beta1, beta2, eps, wd, step):
+    """AdamW for the parameters the pages leave to it (embeddings, norms, scalars).
+
+    The pages name AdamW as Muon's companion for the parameters that are not 2-D
+    non-embedding matrices (notes page setup section 4; recipe page "How to Make Parameter
+    Updates Faster and More Stable?") and give none of its settings.  READING: the usual
+    AdamW with bias correction and decoupled decay, per element in float64 with each
+    operation rounded once, in this order:
+        m = f32(beta1*m + (1-beta1)*g)          (1-beta1) formed in float32
+        v = f32(beta2*v + (1-beta2)*(g*g))
+        bc1 = 1 - beta1^t,  bc2 = 1 - beta2^t   (float64, of the float32 betas)
+        w = f32((1 - lr*wd)*w - (lr*(m/bc1)) / (sqrt(v/bc2) + eps))
+    Returns (W, M, V) as float32.
+    """
+    lr64 = f32(lr)[()]
+    wd64 = f32(wd)[()]
+    b1 = np.float32(beta1)
+    b2 = np.float32(beta2)
+    omb1 = np.float64(np.float32(1.0) - b1)
+    omb2 = np.float64(np.float32(1.0) - b2)
+    b1 = np.float64(b1)
+    b2 = np.float64(b2)
+    eps64 = f32(eps)[()]
+    bc1 = 1.0 - float(b1) ** int(step)
+    bc2 = 1.0 - float(b2) ** int(step)
+    g = np.asarray(G, dtype=np.float64)
+    m = (b1 * np.asarray(M, dtype=np.float32).astype(np.float64) + omb1 * g).astype(np.float32)
+    v = (b2 * np.asarray(V, dtype=np.float32).astype(np.float64) + omb2 * (g * g)).astype(np.float32)
+    mhat = m.astype(np.float64) / bc1
+    vhat = v.astype(np.float64) / bc2
+    den = np.sqrt(vhat) + eps64
+    upd = (lr64 * mhat) / den
+    d = 1.0 - lr64 * wd64
+    w = (d * np.asarray(W, dtype=np.float32).astype(np.float64) - upd).astype(np.float32)
+    return w, m, v
 
 
 def muon_step_ref(W, M, G, *, beta, a, b, c, steps, eps, lr, wd, scale=1.0,

@@ -7,6 +7,7 @@ import ctypes as C
 import os
 import re
 
+import numpy as np
 import pytest
 
 from muon_newton_schulz_momentum_amd import binding as L
@@ -316,3 +317,51 @@ def test_scale_modes_set_each_parameters_update_scale():
     opts = L.muon_plan_opts()
     opts.scale_mode = 7
     assert L.muon_plan_buckets(_descs([(64, 64)]), 1, C.byref(opts), C.byref(p)) == L.MUON_ERR_INVALID_ARG
+
+
+def test_adamw_parameters_are_planned_by_role():
+    mem = FakeMem()
+    shapes = [(64, 128), (4096,), (32000, 64), (300,)]
+    arr = (L.muon_param_desc * 4)()
+    for i, shp in enumerate(shapes):
+        d = arr[i]
+        d.ndim = len(shp)
+        numel = int(np.prod(shp))
+        d.rows, d.cols = (shp if len(shp) == 2 else (numel, 1))
+        d.grad_dtype = L.MUON_DTYPE_F32
+        d.weight, d.momentum, d.grad = mem.take(numel * 4), mem.take(numel * 4), mem.take(numel * 4)
+    arr[1].exp_avg_sq = mem.take(4096 * 4)                   # 1-D with a second moment: AdamW
+    arr[2].exp_avg_sq = mem.take(32000 * 64 * 4)
+    arr[2].optimizer = L.MUON_OPT_ADAMW                      # a 2-D embedding: AdamW
+    # arr[3]: 1-D without a second moment: excluded
+    st, p = _plan(arr)
+    assert st == 0
+    n_chunks, _, n_inc, n_exc = C.c_int32(), None, C.c_int64(), C.c_int64()
+    L.check(L.muon_plan_counts(p, C.byref(n_chunks), None, C.byref(n_inc), C.byref(n_exc)), "counts")
+    assert (n_chunks.value, n_inc.value, n_exc.value) == (1, 1, 1)
+    na, ne = C.c_int64(), C.c_int64()
+    L.check(L.muon_plan_adamw_counts(p, C.byref(na), C.byref(ne)), "adamw counts")
+    assert (na.value, ne.value) == (2, 4096 + 32000 * 64)
+    roles = []
+    for i in range(4):
+        info = L.muon_param_info()
+        L.check(L.muon_plan_param_info(p, i, C.byref(info)), "param_info")
+        roles.append(info.included)
+    assert roles == [1, 2, 2, 0]
+    assert L.muon_plan_validate(p, arr, 4) == 0
+    arr[1].exp_avg_sq = mem.take(4096 * 4)
+    assert L.muon_plan_validate(p, arr, 4) == L.MUON_ERR_STALE_PLAN
+    L.muon_plan_destroy(p)
+    # a second moment overlapping a weight is refused; so is an unknown optimizer
+    arr[1].exp_avg_sq = arr[0].weight
+    assert _plan(arr)[0] == L.MUON_ERR_INVALID_ARG
+    arr[1].exp_avg_sq = mem.take(4096 * 4)
+    arr[3].optimizer = 9
+    assert _plan(arr)[0] == L.MUON_ERR_INVALID_ARG
+    # AdamW refuses an unbound plan and bad settings before touching the device
+    arr[3].optimizer = 0
+    st, p = _plan(arr)
+    k = L.muon_adamw_config()
+    k.lr, k.beta1, k.beta2, k.eps, k.wd, k.step = 1e-3, 0.9, 0.95, 1e-8, 0.1, 1
+    assert L.muon_adamw_step(p, C.byref(k), None) == L.MUON_ERR_NOT_BOUND
+    L.muon_plan_destroy(p)

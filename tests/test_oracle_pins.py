@@ -5,6 +5,7 @@ on tiny inputs, or to values the pages print (tests/golden/), so that a plausibl
 mistake (a dropped term, a wrong sign, a transposed operand, a rounding at the wrong
 place) fails at least one of them.
 """
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -565,3 +566,59 @@ def test_nesterov_lookahead_closed_form_and_rational():
     # beta = 0: the look-ahead is G itself (rounded to bf16)
     _, X = orc.momentum_update(M0, G0, 0.0, nesterov=True)
     np.testing.assert_array_equal(X, orc.bf16_round(G0.astype(np.float64)))
+
+
+# ----------------------------------------------------------------------------------------
+# AdamW companion
+# ----------------------------------------------------------------------------------------
+
+def _r64(x):
+    return Fraction(float(x))          # one float64 rounding of an exact rational
+
+
+def test_adamw_one_step_exact_rational():
+    rng = np.random.default_rng(41)
+    W = (rng.standard_normal(30) * 0.02).astype(np.float32)
+    M = (rng.standard_normal(30) * 1e-3).astype(np.float32)
+    V = np.abs(rng.standard_normal(30) * 1e-6).astype(np.float32)
+    G = (rng.standard_normal(30) * 1e-3).astype(np.float32)
+    lr, b1, b2, eps, wd, t = 1e-3, 0.9, 0.95, 1e-8, 0.1, 7
+    w1, m1, v1 = orc.adamw_update(W, M, V, G, lr=lr, beta1=b1, beta2=b2, eps=eps, wd=wd, step=t)
+    F = lambda v: Fraction(float(np.float32(v)))       # noqa: E731  float32 input, exact
+    lr_, wd_, eps_ = F(lr), F(wd), F(eps)
+    b1_, b2_ = F(b1), F(b2)
+    omb1 = Fraction(float(np.float32(1.0) - np.float32(b1)))
+    omb2 = Fraction(float(np.float32(1.0) - np.float32(b2)))
+    bc1 = _r64(1 - _r64(float(b1_) ** t))
+    bc2 = _r64(1 - _r64(float(b2_) ** t))
+    for w0, m0, v0, g0, wg, mg, vg in zip(W, M, V, G, w1, m1, v1):
+        g = Fraction(float(g0))
+        m = Fraction(float(np.float32(float(_r64(b1_ * Fraction(float(m0)) + omb1 * g)))))
+        sq = _r64(omb2 * (g * g))                       # g*g exact, then one rounding
+        v = Fraction(float(np.float32(float(_r64(b2_ * Fraction(float(v0)) + sq)))))
+        mhat = _r64(m / bc1)
+        vhat = _r64(v / bc2)
+        den = _r64(Fraction(math.sqrt(float(vhat))) + eps_)   # sqrt correctly rounded
+        upd = _r64(_r64(lr_ * mhat) / den)
+        d = _r64(1 - lr_ * wd_)
+        w = float(np.float32(float(_r64(_r64(d * Fraction(float(w0))) - upd))))
+        assert (float(m), float(v), w) == (float(mg), float(vg), float(wg))
+
+
+def test_adamw_first_step_closed_form():
+    # t = 1 from zero moments: m/bc1 = g and v/bc2 = g^2 up to roundings, so the update is
+    # lr * g / (|g| + eps): a sign step of size lr for |g| >> eps
+    rng = np.random.default_rng(42)
+    G = (rng.standard_normal(200) * 1e-2).astype(np.float32)
+    W = (rng.standard_normal(200) * 0.02).astype(np.float32)
+    Z = np.zeros_like(G)
+    lr, wd = 1e-3, 0.0
+    w1, m1, v1 = orc.adamw_update(W, Z, Z, G, lr=lr, beta1=0.9, beta2=0.999, eps=1e-12, wd=wd, step=1)
+    lr32 = float(np.float32(lr))
+    np.testing.assert_allclose(w1.astype(np.float64), W.astype(np.float64) - lr32 * np.sign(G),
+                               rtol=0, atol=4e-9)
+    np.testing.assert_allclose(m1, (1 - np.float32(0.9)) * G, rtol=1e-6)
+    np.testing.assert_allclose(v1, (1 - np.float32(0.999)) * G.astype(np.float64) ** 2, rtol=1e-6)
+    # lr = 0 and wd = 0 leave W untouched whatever the moments
+    w0, _, _ = orc.adamw_update(W, m1, v1, G, lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0, step=3)
+    np.testing.assert_array_equal(w0, W)
