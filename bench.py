@@ -79,6 +79,11 @@ def main(argv=None):
     ap.add_argument("--max-workspace-gib", type=float, default=-1.0,
                     help="workspace cap in GiB (0: none; default: none if it fits next to the inputs, "
                          "else 8 GiB chunks)")
+    ap.add_argument("--pipeline", type=int, choices=(0, 1), default=1,
+                    help="1: the two-stream step (side-stream elementwise kernels beside the NS products)")
+    ap.add_argument("--adamw-elements", type=int, default=0,
+                    help="also update one AdamW parameter of this many float32 elements (an embedding "
+                         "table) inside every step")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -104,6 +109,17 @@ def main(argv=None):
     w = wl.get(args.workload)
     t0 = time.time()
     params = harness.make_params(w, device="cuda")
+    adamw_cfg = None
+    if args.adamw_elements > 0:
+        n_el = args.adamw_elements
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(wl.seed_of(w.cid, len(w.params), 9))
+        emb = harness.ParamTensors(torch.randn(n_el, generator=gen, device="cuda") * 0.02,
+                                   torch.zeros(n_el, device="cuda"),
+                                   torch.randn(n_el, generator=gen, device="cuda") * 1e-3,
+                                   exp_avg_sq=torch.zeros(n_el, device="cuda"))
+        params.append(emb)
+        adamw_cfg = harness.Plan.adamw_config(3e-4, 0.9, 0.95, 1e-8, 0.1, 1)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
 
@@ -135,14 +151,17 @@ def main(argv=None):
         free, _ = torch.cuda.mem_get_info()
         if need > free - (4 << 30):
             cap = 8 << 30
-    plan = harness.Plan(params, max_workspace_bytes=cap)
+    plan = harness.Plan(params, max_workspace_bytes=cap,
+                        flags=L.MUON_PLAN_DOUBLE_BUFFER if (cap and args.pipeline) else 0)
     stream = torch.cuda.current_stream()
+    kw = dict(a=w.a, b=w.b, c=w.c, steps=w.steps, eps=w.eps, adamw=adamw_cfg)
 
-    def step():
-        plan.step(w.beta, w.lr, w.wd, w.a, w.b, w.c, w.steps, w.eps)
+    def step(pipeline):
+        plan.step_ex(w.beta, w.lr, w.wd, pipeline=pipeline, **kw)
 
-    # first warm-up step (eager): its outputs are the sampled parity check
-    step()
+    # first warm-up step (eager, in the timed configuration): its outputs are the sampled
+    # parity check
+    step(bool(args.pipeline))
     torch.cuda.synchronize()
     first = {}
     for i in snap:
@@ -150,7 +169,7 @@ def main(argv=None):
                     params[i].momentum.cpu().numpy(), params[i].weight.cpu().numpy())
 
     # the step as one graph; the remaining warm-up steps are replays of it
-    graph = plan.capture(w.beta, w.lr, w.wd, w.a, w.b, w.c, w.steps, w.eps)
+    graph = plan.capture_ex(w.beta, w.lr, w.wd, pipeline=bool(args.pipeline), **kw)
     for _ in range(args.warmup - 1):
         graph.launch(stream)
     torch.cuda.synchronize()
@@ -170,14 +189,14 @@ def main(argv=None):
     graph_nodes = graph.nodes
     graph.close()
 
-    # ---- kernel timing: K more steps launched one kernel at a time, each kernel between
-    # a HIP event pair recorded on its own launch stream --------------------------------
-    launches_per_step = plan.n_chunks * (4 + 3 * w.steps)
+    # ---- kernel timing: K more steps launched one kernel at a time on one stream (so that
+    # no two kernels overlap), each kernel between a HIP event pair ---------------------
+    launches_per_step = plan.n_chunks * (4 + 3 * w.steps) + 1
     plan.timing_enable(launches_per_step * args.steps + 16)
     torch.cuda.synchronize()
     t_eager = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(False)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t_eager) * 1e3 / args.steps
 
@@ -204,7 +223,7 @@ def main(argv=None):
         "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
         "frac": round(dk["frac"], 4), "traffic": load_traffic(dom, w.key),
         "work_per_launch": dk["work_per_launch"], "mean_launch_ms": dk["mean_launch_ms"],
-        "measured_over": f"{args.steps} steps launched kernel by kernel right after the timed graph replays",
+        "measured_over": f"{args.steps} steps launched kernel by kernel on one stream right after the timed graph replays",
     }
 
     conv, alg = w.ns_flops()
@@ -273,6 +292,7 @@ def main(argv=None):
             "workspace_gib": round(plan.workspace_bytes / (1 << 30), 3),
             "ns_iterations": w.steps, "coefficients": [w.a, w.b, w.c], "beta": w.beta,
             "lr": w.lr, "wd": w.wd, "parallelism": "single GPU",
+            "streams": "two (pipeline)" if args.pipeline else "one",
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

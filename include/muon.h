@@ -104,7 +104,7 @@ typedef struct muon_plan_opts {
      * descriptors; entries of excluded parameters are ignored).  NULL means s_i = 1.
      * The pages give no scale rule; the scale is a free per-matrix factor. */
     const float* scale;
-    /* MUON_PLAN_* bits; 0 for the defaults. */
+    /* MUON_PLAN_* bits; 0 for the defaults.  Other bits: INVALID_ARG. */
     uint32_t flags;
     /* Update-scale rule used where `scale` is NULL (MUON_SCALE_*).  The pages give no
      * rule: one of them notes only that careful per-parameter scaling of the update
@@ -127,6 +127,13 @@ typedef struct muon_plan_opts {
 /* Orthogonalise small matrices with the tiled kernels too, instead of the fused
  * whole-iteration kernel (both give bitwise the same result; this exists to show it). */
 #define MUON_PLAN_TILED_SMALL 1u
+/* With a workspace cap that splits buckets into chunks: lay the chunks out in two regions
+ * of at most half the remaining cap each, alternating between consecutive tiled chunks,
+ * so that the two-stream pipeline (muon_step_config.pipeline) can prepare one chunk while
+ * the previous one is orthogonalised.  Chunks hold about half as many matrices.  No
+ * effect without a cap, or when everything fits under it (every chunk then has its own
+ * region). */
+#define MUON_PLAN_DOUBLE_BUFFER 2u
 
 typedef struct muon_plan muon_plan;
 
@@ -287,11 +294,24 @@ typedef struct muon_step_config {
     /* Host, nullable: also run AdamW over the plan's AdamW parameters (after the Muon
      * step, on the same stream), so one call updates every parameter. */
     const muon_adamw_config* adamw;
+    /* 0: one stream, phase by phase.  1: the two-stream pipeline, for whole steps
+     * (chunk -1): while one chunk's Newton–Schulz products run on `stream`, the next
+     * chunk's momentum and normaliser and the previous chunk's apply run on a second
+     * stream that the plan owns (created at bind, default priority), in kernels small
+     * enough to share the compute units with the products; the call returns with all of
+     * it ordered before later work on `stream`.  The pages overlap the next batch's
+     * exchange with the current batch's orthogonalisation ("Frontier Pre-training at
+     * Microsoft AI", method details section 5, "Scaling Muon to 16K GPUs").  Results are
+     * bitwise those of 0.  It needs at least two tiled chunks, no two consecutive ones
+     * in one workspace region (always so without a binding cap; with one, plan with
+     * MUON_PLAN_DOUBLE_BUFFER); otherwise the step runs as with 0.  Steps of one plan
+     * must not overlap: the second stream is shared by every call on the plan. */
+    int32_t pipeline;
 } muon_step_config;
 
 /* muon_step with a muon_step_config.  Errors: INVALID_ARG (NULL config, chunk, steps,
- * non-finite scalars or coefficients, nesterov not 0/1), ALIGNMENT (dev_scalars),
- * NOT_BOUND, HIP. */
+ * non-finite scalars or coefficients, nesterov or pipeline not 0/1), ALIGNMENT
+ * (dev_scalars), NOT_BOUND, HIP. */
 MUON_API muon_status muon_step_ex(const muon_plan* plan, int32_t chunk, const muon_step_config* config,
                          void* stream);
 

@@ -52,6 +52,7 @@ MUON_OPT_ADAMW = 1
 MUON_OPT_NONE = 2
 
 MUON_PLAN_TILED_SMALL = 1
+MUON_PLAN_DOUBLE_BUFFER = 2
 
 MUON_SCALE_NONE = 0
 MUON_SCALE_ASPECT = 1
@@ -89,7 +90,7 @@ class muon_step_config(C.Structure):
     _fields_ = [("beta", C.c_float), ("lr", C.c_float), ("wd", C.c_float), ("eps", C.c_float),
                 ("steps", C.c_int32), ("a", C.c_float), ("b", C.c_float), ("c", C.c_float),
                 ("coeffs", C.POINTER(C.c_float)), ("nesterov", C.c_int32), ("dev_scalars", C.c_void_p),
-                ("adamw", C.POINTER(muon_adamw_config))]
+                ("adamw", C.POINTER(muon_adamw_config)), ("pipeline", C.c_int32)]
 
 
 class muon_param_info(C.Structure):

@@ -68,6 +68,7 @@ struct StepCfg {
     const float* dev = nullptr;      // device {beta, lr, wd}, read by the kernels when set
     bool adam = false;               // also run AdamW with `adam_args`
     AdamArgs adam_args{};
+    bool pipeline = false;           // the two-stream order (step_pipelined)
 };
 
 // AdamW launch arguments from the public config (validated); tables filled in at launch.
@@ -132,7 +133,12 @@ muon_status check_ns(int32_t steps, const float* abc, float eps, const char* who
 
 // ---- the three steps for one chunk --------------------------------------------------------
 
-muon_status momentum_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, hipStream_t s) {
+// Chunks whose matrices have fewer than 2^30 elements may use the side-stream kernels
+// (their byte offsets are 32-bit).
+bool side_ok(const Chunk& c) { return c.m * c.n < (int64_t(1) << 30); }
+
+muon_status momentum_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, hipStream_t s,
+                           bool side = false) {
     MomentumArgs a;
     a.tbl = at<const MatEntry>(p, c.off_table);
     a.xq = at<uint16_t>(p, c.off_xq);
@@ -147,20 +153,25 @@ muon_status momentum_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cf
     a.nesterov = cfg.nesterov ? 1 : 0;
     const double gsz = c.grad_dtype == MUON_DTYPE_F32 ? 4.0 : 2.0;
     TimedLaunch tl(p, MUON_KERNEL_MOMENTUM, (double)c.count * c.m * c.n * (10.0 + gsz), s);
-    const hipError_t e = launch_momentum(a, c.grad_dtype, s);
+    const hipError_t e = (side && side_ok(c)) ? launch_momentum_side(a, c.grad_dtype, s)
+                                              : launch_momentum(a, c.grad_dtype, s);
     tl.done(s);
     return e == hipSuccess ? MUON_OK : hip_fail(e, "momentum kernel launch");
 }
 
-muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, float eps,
-                     hipStream_t s) {
-    uint16_t* xp = at<uint16_t>(p, c.off_xp);
+// The X buffer the iteration starts in.  It ping-pongs between the two X buffers and must
+// end in xp, where the apply step reads O: start in xq (normalised in place) for an odd
+// step count.
+uint16_t* ns_start(const muon_plan* p, const Chunk& c, int32_t steps) {
+    return (steps & 1) ? at<uint16_t>(p, c.off_xq) : at<uint16_t>(p, c.off_xp);
+}
+
+// Step 2 for a chunk: the normaliser from the momentum kernel's partial sums, then
+// X = bf16(X0 / (||X0|| + eps)) into the starting buffer.
+muon_status ns_prep(const muon_plan* p, const Chunk& c, int32_t steps, float eps, hipStream_t s, bool side = false) {
     uint16_t* xq = at<uint16_t>(p, c.off_xq);
-    uint16_t* am = at<uint16_t>(p, c.off_a);
-    uint16_t* bm = at<uint16_t>(p, c.off_b);
     double* inv = at<double>(p, c.off_inv);
     hipError_t e;
-
     {
         FinalizeArgs f{at<const double>(p, c.off_part), inv, c.ew_tiles, (double)eps};
         TimedLaunch tl(p, MUON_KERNEL_NORM_FINALIZE, (double)c.count * c.ew_tiles * 8.0, s);
@@ -168,16 +179,24 @@ muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32
         tl.done(s);
         if (e != hipSuccess) return hip_fail(e, "norm finalize kernel launch");
     }
-    // The iteration ping-pongs between the two X buffers and must end in xp, where the
-    // apply step reads O: start in xq (normalised in place) for an odd step count.
-    uint16_t* cur = (steps & 1) ? xq : xp;
     {
-        NormalizeArgs n{xq, cur, inv, c.m, c.n, c.mp, c.np, c.count * c.mp * c.np / 8};
+        NormalizeArgs n{xq, ns_start(p, c, steps), inv, c.m, c.n, c.mp, c.np, c.count * c.mp * c.np / 8};
         TimedLaunch tl(p, MUON_KERNEL_NORMALIZE, (double)c.count * c.m * c.n * 4.0, s);
-        e = launch_normalize(n, s);
+        e = side ? launch_normalize_side(n, s) : launch_normalize(n, s);
         tl.done(s);
         if (e != hipSuccess) return hip_fail(e, "normalize kernel launch");
     }
+    return MUON_OK;
+}
+
+// Step 3 for a chunk: the iterations, from the normalised X.
+muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, hipStream_t s) {
+    uint16_t* xp = at<uint16_t>(p, c.off_xp);
+    uint16_t* xq = at<uint16_t>(p, c.off_xq);
+    uint16_t* am = at<uint16_t>(p, c.off_a);
+    uint16_t* bm = at<uint16_t>(p, c.off_b);
+    uint16_t* cur = ns_start(p, c, steps);
+    hipError_t e;
 
     const int32_t tile = c.tile;
     const int32_t tm = (int32_t)(c.mp / tile), tn = (int32_t)(c.np / tile);
@@ -227,6 +246,12 @@ muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32
         cur = nxt;
     }
     return MUON_OK;
+}
+
+muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, float eps,
+                     hipStream_t s) {
+    const muon_status st = ns_prep(p, c, steps, eps, s);
+    return st != MUON_OK ? st : ns_iterate(p, c, abc, steps, s);
 }
 
 // Algorithmic FLOPs of one Newton–Schulz iteration over a chunk (the three products,
@@ -301,7 +326,8 @@ muon_status ns_all(const muon_plan* p, const float* abc, int32_t steps, float ep
     return MUON_OK;
 }
 
-muon_status apply_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, hipStream_t s) {
+muon_status apply_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, hipStream_t s,
+                        bool side = false) {
     ApplyArgs a;
     a.tbl = at<const MatEntry>(p, c.off_table);
     a.xo = at<const uint16_t>(p, c.off_xp);
@@ -314,18 +340,108 @@ muon_status apply_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, 
     a.lr = cfg.lr;
     a.dev_scalars = cfg.dev;
     TimedLaunch tl(p, MUON_KERNEL_APPLY, (double)c.count * c.m * c.n * 10.0, s);
-    const hipError_t e = launch_apply(a, s);
+    const hipError_t e = (side && side_ok(c)) ? launch_apply_side(a, s) : launch_apply(a, s);
     tl.done(s);
     return e == hipSuccess ? MUON_OK : hip_fail(e, "apply kernel launch");
 }
 
+hipError_t record(const muon_plan* p, size_t k, hipStream_t s) {
+    return hipEventRecord((hipEvent_t)p->pipe_events[k], s);
+}
+hipError_t wait(const muon_plan* p, size_t k, hipStream_t s) {
+    return hipStreamWaitEvent(s, (hipEvent_t)p->pipe_events[k], 0);
+}
+
+// The tiled chunks, in plan order, when the two-stream pipeline can run them: at least two,
+// and no two consecutive ones in the same workspace region.  Empty otherwise.
+std::vector<int32_t> pipeline_chunks(const muon_plan* p) {
+    std::vector<int32_t> t;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
+        if (!p->chunks[(size_t)i].fused) t.push_back(i);
+    if (t.size() < 2 || !p->side || p->pipe_events.size() < 2 + 2 * t.size()) return {};
+    for (size_t j = 1; j < t.size(); ++j)
+        if (p->chunks[(size_t)t[j]].region_off == p->chunks[(size_t)t[j - 1]].region_off) return {};
+    return t;
+}
+
+// The whole step with two streams.  The pages overlap the exchange of the next batch of
+// matrices with the orthogonalisation of the current one ("Frontier Pre-training at
+// Microsoft AI", method details section 5, "Scaling Muon to 16K GPUs", the prefetching of
+// the next batch).  On one GPU the work beside the products is the HBM-bound part of the
+// step: chunk j+1's momentum and normaliser and chunk j-1's apply run on the plan's side
+// stream while chunk j's Newton–Schulz products run on the caller's stream, in the
+// side-stream kernels sized to share each compute unit with a product workgroup.
+//
+// Order, for the tiled chunks u_0 .. u_{T-1} (small fused chunks first, as in the
+// one-stream order, on the caller's stream s):
+//   s: momentum(u_0), prep(u_0), [fork], NS(u_0), [wait prep(u_1)], NS(u_1), ...,
+//      NS(u_{T-1}), apply(u_{T-1}), [join]
+//   d: momentum(u_1), prep(u_1), [wait NS(u_0)], apply(u_0), momentum(u_2), prep(u_2),
+//      [wait NS(u_1)], apply(u_1), ...
+// Consecutive tiled chunks are in different regions, so what runs side by side never
+// touches the same workspace bytes; u_{j+1}'s momentum runs after u_{j-1}'s apply on d,
+// so two regions are enough.  Events: 0 fork, 1 join, 2 + j prep(u_j) done, 2 + T + j
+// NS(u_j) done.
+muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, const StepCfg& cfg, hipStream_t s) {
+    muon_status st;
+    hipError_t e = hipSuccess;
+    const float* abc = cfg.abc.data();
+    const size_t T = u.size();
+    hipStream_t d = (hipStream_t)p->side;
+
+    std::vector<int32_t> small;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
+        if (p->chunks[(size_t)i].fused) small.push_back(i);
+    if (!p->shared_regions) {
+        for (int32_t i : small)
+            if ((st = momentum_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
+        if ((st = ns_small_chunks(p, small, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+        for (int32_t i : small)
+            if ((st = apply_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
+    } else {
+        for (int32_t i : small) {
+            const Chunk& ch = p->chunks[(size_t)i];
+            if ((st = momentum_chunk(p, ch, cfg, s)) != MUON_OK) return st;
+            if ((st = ns_one(p, i, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+            if ((st = apply_chunk(p, ch, cfg, s)) != MUON_OK) return st;
+        }
+    }
+
+    const Chunk& c0 = p->chunks[(size_t)u[0]];
+    if ((st = momentum_chunk(p, c0, cfg, s)) != MUON_OK) return st;
+    if ((st = ns_prep(p, c0, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+    if ((e = record(p, 0, s)) != hipSuccess || (e = wait(p, 0, d)) != hipSuccess)
+        return hip_fail(e, "pipeline fork");
+    for (size_t j = 0; j < T; ++j) {
+        const Chunk& cj = p->chunks[(size_t)u[j]];
+        if (j > 0 && (e = wait(p, 2 + j, s)) != hipSuccess) return hip_fail(e, "pipeline wait");
+        if ((st = ns_iterate(p, cj, abc, cfg.steps, s)) != MUON_OK) return st;
+        if (j + 1 == T) break;
+        if ((e = record(p, 2 + T + j, s)) != hipSuccess) return hip_fail(e, "pipeline record");
+        const Chunk& cn = p->chunks[(size_t)u[j + 1]];
+        if ((st = momentum_chunk(p, cn, cfg, d, true)) != MUON_OK) return st;
+        if ((st = ns_prep(p, cn, cfg.steps, cfg.eps, d, true)) != MUON_OK) return st;
+        if ((e = record(p, 2 + j + 1, d)) != hipSuccess || (e = wait(p, 2 + T + j, d)) != hipSuccess)
+            return hip_fail(e, "pipeline record");
+        if ((st = apply_chunk(p, cj, cfg, d, true)) != MUON_OK) return st;
+    }
+    if ((st = apply_chunk(p, p->chunks[(size_t)u[T - 1]], cfg, s)) != MUON_OK) return st;
+    if ((e = record(p, 1, d)) != hipSuccess || (e = wait(p, 1, s)) != hipSuccess) return hip_fail(e, "pipeline join");
+    return cfg.adam ? adam_run(p, cfg.adam_args, s) : MUON_OK;
+}
+
 // Steps 1, 3 and 5 for one chunk, or for every chunk (-1) on one stream.  With distinct
 // regions every chunk's momentum runs first, then Newton–Schulz (small chunks grouped),
-// then every apply; chunks that share a region go through all three in turn.
+// then every apply; chunks that share a region go through all three in turn.  With
+// `pipeline` (every chunk), the two-stream order above where the plan allows it.
 muon_status step_chunks(const muon_plan* p, int32_t chunk, const StepCfg& cfg, hipStream_t s) {
     muon_status st;
     const int32_t nc = (int32_t)p->chunks.size();
     const float* abc = cfg.abc.data();
+    if (chunk == -1 && cfg.pipeline) {
+        const std::vector<int32_t> u = pipeline_chunks(p);
+        if (!u.empty()) return step_pipelined(p, u, cfg, s);
+    }
     if (chunk == -1 && !p->shared_regions) {
         for (int32_t i = 0; i < nc; ++i)
             if ((st = momentum_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
@@ -367,6 +483,9 @@ muon_status make_cfg(const muon_step_config* c, StepCfg& cfg, const char* who) {
     cfg.eps = c->eps;
     cfg.nesterov = c->nesterov == 1;
     cfg.dev = c->dev_scalars;
+    if (c->pipeline != 0 && c->pipeline != 1)
+        return set_error(MUON_ERR_INVALID_ARG, std::string(who) + ": pipeline must be 0 or 1");
+    cfg.pipeline = c->pipeline == 1;
     if (c->adamw) {
         if ((st = make_adam(c->adamw, cfg.adam_args, who)) != MUON_OK) return st;
         cfg.adam = true;
@@ -398,6 +517,10 @@ void muon_internal_release(muon_plan* p) {
     for (void* ev : p->timing.ev_begin) (void)hipEventDestroy((hipEvent_t)ev);
     for (void* ev : p->timing.ev_end) (void)hipEventDestroy((hipEvent_t)ev);
     p->timing = TimingState{};
+    for (void* ev : p->pipe_events) (void)hipEventDestroy((hipEvent_t)ev);
+    p->pipe_events.clear();
+    if (p->side) (void)hipStreamDestroy((hipStream_t)p->side);
+    p->side = nullptr;
 }
 
 muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream) {
@@ -429,6 +552,20 @@ muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream)
         // consumed it before the caller can free or change anything
         e = hipStreamSynchronize(s);
         if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: stream synchronize");
+    }
+    // the two-stream pipeline's side stream (default priority) and ordering events, made
+    // here so that no step has to create anything (a step may be under graph capture)
+    if (!p->side) {
+        hipStream_t side = nullptr;
+        e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+        if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipStreamCreateWithFlags");
+        p->side = side;
+    }
+    while (p->pipe_events.size() < 2 + 2 * p->chunks.size()) {
+        hipEvent_t ev = nullptr;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipEventCreateWithFlags");
+        p->pipe_events.push_back(ev);
     }
     p->ws = ws;
     p->ws_given = bytes;

@@ -456,6 +456,360 @@ __global__ __launch_bounds__(256) void apply_kernel(ApplyArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Side-stream variants of the momentum, normalise and apply kernels.  While one chunk's
+// Newton–Schulz products hold the compute units, the next chunk's momentum and
+// normalisation and the previous chunk's apply run beside them on a second stream.  A
+// product workgroup (8 waves of at most 232 VGPRs, 2 per SIMD, and about 128.5 KB of LDS)
+// leaves 48 VGPRs per SIMD lane and 31.5 KB of LDS free on its CU: these kernels stay
+// within that (one 16-byte unit per lane per pass, no arrays of loads in flight) and are
+// launched with one workgroup per CU, so that every CU holds one product workgroup and one
+// of these at once instead of the two waiting for each other.
+//
+// Their results are bitwise those of the kernels above: the same per-element arithmetic,
+// the same tile-to-element mapping, and the momentum's sums of squares accumulated per
+// tile in the same order (unit by unit, element by element, then the fixed block order).
+// ---------------------------------------------------------------------------------------
+// A wave-uniform double moved to scalar registers (VALU float64 instructions take it from
+// there, which keeps two VGPR pairs free in the side kernels).
+__device__ __forceinline__ double uniform_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// A wave-uniform 64-bit integer moved to scalar registers: the 64-bit division that finds a
+// tile's matrix is expanded into vector instructions, and the table row and buffer
+// resources built from its result must stay scalar.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// A table row with every field in scalar registers.  The row is read with vector loads (the
+// compiler cannot tell that the kernel's stores leave the table alone, so the scalar cache
+// is not used); buffer resources built from vector-register values would be executed in
+// per-lane loops.
+__device__ __forceinline__ MatEntry uniform_entry(const MatEntry* tbl, int64_t mat) {
+    const MatEntry v = tbl[mat];
+    MatEntry e{};
+    e.w = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(v.w)));
+    e.m = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(v.m)));
+    e.g = reinterpret_cast<const void*>(uniform_i64(reinterpret_cast<int64_t>(v.g)));
+    e.rows = uniform_i64(v.rows);
+    e.cols = uniform_i64(v.cols);
+    e.trans = (int32_t)__builtin_amdgcn_readfirstlane((uint32_t)v.trans);
+    e.scale = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(v.scale)));
+    return e;
+}
+
+// Four momentum elements and their NS inputs, one element after another: the scheduling
+// barriers keep the four float64 chains from being interleaved, which would take more
+// registers than the side kernels have.
+__device__ __forceinline__ void momentum4_serial(float4& mn, uint16_t xb[4], float4 mv, const float gv[4], bool nest,
+                                                 double beta, double omb) {
+    mn.x = momentum_elem(mv.x, gv[0], beta, omb);
+    xb[0] = x0_bits(mn.x, gv[0], nest, beta, omb);
+    __builtin_amdgcn_sched_barrier(0);
+    mn.y = momentum_elem(mv.y, gv[1], beta, omb);
+    xb[1] = x0_bits(mn.y, gv[1], nest, beta, omb);
+    __builtin_amdgcn_sched_barrier(0);
+    mn.z = momentum_elem(mv.z, gv[2], beta, omb);
+    xb[2] = x0_bits(mn.z, gv[2], nest, beta, omb);
+    __builtin_amdgcn_sched_barrier(0);
+    mn.w = momentum_elem(mv.w, gv[3], beta, omb);
+    xb[3] = x0_bits(mn.w, gv[3], nest, beta, omb);
+}
+
+// Buffer accesses for the side kernels: a scalar resource per array and a 32-bit byte
+// offset per lane (a generic pointer would need a 64-bit address per lane).  A chunk goes
+// to these kernels only when its matrices have fewer than 2^30 elements, so every byte
+// offset below fits 32 bits.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t side_rsrc(const void* base, uint64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)bytes, 0x00020000);
+}
+__device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ __forceinline__ void st_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 f) {
+    u32x4 v;
+    v.x = __float_as_uint(f.x); v.y = __float_as_uint(f.y); v.z = __float_as_uint(f.z); v.w = __float_as_uint(f.w);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+// Four gradient elements starting at element i, widened to float32.
+template <int GDT>
+__device__ __forceinline__ void side_grad4(__amdgpu_buffer_rsrc_t rg, uint32_t i, float out[4]) {
+    if (GDT == MUON_DTYPE_F32) {
+        const float4 v = ld_f4(rg, i * 4u);
+        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    } else {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rg, i * 2u, 0, 0);
+        out[0] = bf16_to_f32(v.x & 0xffffu); out[1] = bf16_to_f32(v.x >> 16);
+        out[2] = bf16_to_f32(v.y & 0xffffu); out[3] = bf16_to_f32(v.y >> 16);
+    }
+}
+template <int GDT>
+__device__ __forceinline__ float side_grad1(__amdgpu_buffer_rsrc_t rg, uint32_t i) {
+    if (GDT == MUON_DTYPE_F32) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, i * 4u, 0, 0));
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, i * 2u, 0, 0));
+}
+
+template <int GDT>
+__global__ __launch_bounds__(256) void momentum_side_kernel(MomentumArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t tr[T][LDT];
+    __shared__ double red[4];
+    const int tid = threadIdx.x;
+    const int cg = tid & 15, rg = tid >> 4;
+    float beta32 = a.beta, omb32 = a.omb;
+    if (a.dev_scalars) {
+        beta32 = a.dev_scalars[0];
+        omb32 = 1.0f - beta32;
+    }
+    const double beta = uniform_f64((double)beta32), omb = uniform_f64((double)omb32);
+    const bool nest = a.nesterov != 0;
+    const uint32_t np = (uint32_t)a.np;
+
+    for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        const int64_t mat = uniform_i64(t / a.ew_tiles);
+        const uint32_t tile = (uint32_t)(t - mat * a.ew_tiles);
+        const MatEntry e = uniform_entry(a.tbl, mat);
+        const uint32_t rows = (uint32_t)e.rows, cols = (uint32_t)e.cols;
+        const uint32_t nel = rows * cols;
+        const bool vec = (cols & 3) == 0;
+        const __amdgpu_buffer_rsrc_t rm = side_rsrc(e.m, (uint64_t)nel * 4);
+        const __amdgpu_buffer_rsrc_t rgr = side_rsrc(e.g, (uint64_t)nel * (GDT == MUON_DTYPE_F32 ? 4 : 2));
+        const __amdgpu_buffer_rsrc_t rx = side_rsrc(a.xq + mat * a.mat_stride, (uint64_t)a.mat_stride * 2);
+        double ss = 0.0;
+        if (!e.trans && vec && (np & 3) == 0) {
+            // flat, as in momentum_kernel
+            const uint32_t e0 = tile * (T * T) + (uint32_t)tid * 4u;
+#pragma unroll 1
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t idx = e0 + (uint32_t)k * 1024u;
+                if (idx >= nel) break;
+                const float4 mv = ld_f4(rm, idx * 4u);
+                float gv[4];
+                side_grad4<GDT>(rgr, idx, gv);
+                float4 mn;
+                uint16_t xb[4];
+                momentum4_serial(mn, xb, mv, gv, nest, beta, omb);
+                st_f4(rm, idx * 4u, mn);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const double x = (double)bf16_to_f32(xb[j]);
+                    ss += x * x;
+                }
+                const uint32_t xi = (np == cols) ? idx : (idx / cols) * np + idx % cols;
+                u32x2 v;
+                v.x = (uint32_t)xb[0] | ((uint32_t)xb[1] << 16);
+                v.y = (uint32_t)xb[2] | ((uint32_t)xb[3] << 16);
+                __builtin_amdgcn_raw_buffer_store_b64(v, rx, xi * 2u, 0, 0);
+            }
+        } else {
+            // 2-D tile, as momentum_kernel's general loop
+            const uint32_t tiles_c = (cols + T - 1) / T;
+            const uint32_t r0 = (tile / tiles_c) * T, c0 = (tile % tiles_c) * T;
+            const uint32_t c = c0 + (uint32_t)cg * 4u;
+            const int nvalid = c >= cols ? 0 : (cols - c < 4 ? (int)(cols - c) : 4);
+            const bool v4 = vec && nvalid == 4;
+#pragma unroll 1
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t r = r0 + (uint32_t)rg + 16u * (uint32_t)i;
+                uint16_t xb[4] = {0, 0, 0, 0};
+                const bool live = r < rows && nvalid > 0;
+                if (live) {
+                    const uint32_t base = r * cols + c;
+                    if (v4) {
+                        const float4 mv = ld_f4(rm, base * 4u);
+                        float gv[4];
+                        side_grad4<GDT>(rgr, base, gv);
+                        float4 mn;
+                        momentum4_serial(mn, xb, mv, gv, nest, beta, omb);
+                        st_f4(rm, base * 4u, mn);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            if (j < nvalid) {
+                                const uint32_t q = (base + (uint32_t)j) * 4u;
+                                const float gj = side_grad1<GDT>(rgr, base + (uint32_t)j);
+                                const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, q, 0, 0));
+                                const float mn = momentum_elem(m0, gj, beta, omb);
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mn), rm, q, 0, 0);
+                                xb[j] = x0_bits(mn, gj, nest, beta, omb);
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const double x = (double)bf16_to_f32(xb[j]);
+                        ss += x * x;
+                    }
+                }
+                if (!e.trans) {
+                    if (live) {
+                        const uint32_t xo = (r * np + c) * 2u;
+                        if (nvalid == 4 && (np & 3) == 0) {
+                            u32x2 v;
+                            v.x = (uint32_t)xb[0] | ((uint32_t)xb[1] << 16);
+                            v.y = (uint32_t)xb[2] | ((uint32_t)xb[3] << 16);
+                            __builtin_amdgcn_raw_buffer_store_b64(v, rx, xo, 0, 0);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                if (j < nvalid) __builtin_amdgcn_raw_buffer_store_b16(xb[j], rx, xo + 2u * (uint32_t)j, 0, 0);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) tr[cg * 4 + j][rg + 16 * i] = xb[j];
+                }
+            }
+            if (e.trans) {
+                // X0 = M^T: row q of the block is column c0 + q of M
+                __syncthreads();
+                const int q = tid >> 2, seg = (tid & 3) * 16;
+                const uint32_t xr = c0 + (uint32_t)q;
+                const uint32_t xc = r0 + (uint32_t)seg;
+                if (xr < cols && xc < rows) {
+                    const uint32_t xo = (xr * np + xc) * 2u;
+                    if (xc + 16 <= rows) {
+                        const u32x4* srcv = reinterpret_cast<const u32x4*>(&tr[q][seg]);
+                        __builtin_amdgcn_raw_buffer_store_b128(srcv[0], rx, xo, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(srcv[1], rx, xo + 16u, 0, 0);
+                    } else {
+                        for (uint32_t k = 0; xc + k < rows; ++k)
+                            __builtin_amdgcn_raw_buffer_store_b16(tr[q][seg + k], rx, xo + 2u * k, 0, 0);
+                    }
+                }
+            }
+        }
+        ss = dev::wave_sum(ss);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        if (tid == 0) a.partials[t] = (red[0] + red[1]) + (red[2] + red[3]);
+        __syncthreads();
+    }
+}
+
+// One 8-element unit per thread and pass (normalize_kernel takes UPT at a time).
+__global__ __launch_bounds__(256) void normalize_side_kernel(NormalizeArgs a) {
+    const int64_t upr = a.np >> 3;
+    const int64_t per_mat = a.mp * upr;
+    const int64_t span = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < a.total_units; u += span) {
+        const int64_t mat = u / per_mat;
+        const int64_t rem = u - mat * per_mat;
+        const int64_t r = rem / upr;
+        const int64_t c = (rem - r * upr) * 8;
+        const int64_t off = mat * a.mp * a.np + r * a.np + c;
+        uint4 out = make_uint4(0, 0, 0, 0);
+        if (r < a.m && c < a.n)
+            out = normalize_unit(*reinterpret_cast<const uint4*>(a.src + off), c, a.n, a.inv[mat]);
+        *reinterpret_cast<uint4*>(a.dst + off) = out;
+    }
+}
+
+// Four apply elements one after another (see momentum4_serial).
+__device__ __forceinline__ void apply4_serial(float4& w, const float o[4], double d, double u) {
+    w.x = apply_elem(w.x, o[0], d, u);
+    __builtin_amdgcn_sched_barrier(0);
+    w.y = apply_elem(w.y, o[1], d, u);
+    __builtin_amdgcn_sched_barrier(0);
+    w.z = apply_elem(w.z, o[2], d, u);
+    __builtin_amdgcn_sched_barrier(0);
+    w.w = apply_elem(w.w, o[3], d, u);
+}
+
+__global__ __launch_bounds__(256) void apply_side_kernel(ApplyArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t tr[T][LDT];
+    const int tid = threadIdx.x;
+    const int cg = tid & 15, rg = tid >> 4;
+    if (a.dev_scalars) {
+        const float lr = a.dev_scalars[1], wd = a.dev_scalars[2];
+        a.lr = lr;
+        a.d = 1.0 - (double)lr * (double)wd;
+    }
+    const double d = uniform_f64(a.d);
+
+    for (int64_t t = blockIdx.x; t < a.total_tiles; t += gridDim.x) {
+        const int64_t mat = uniform_i64(t / a.ew_tiles);
+        const int64_t tile = t - mat * a.ew_tiles;
+        const MatEntry e = uniform_entry(a.tbl, mat);
+        const bool vec = (e.cols & 3) == 0;
+        const uint16_t* O = a.xo + mat * a.mat_stride;
+        const double u = uniform_f64((double)a.lr * (double)e.scale);
+        if (!e.trans && vec && (a.np & 3) == 0) {
+            const uint32_t nel = (uint32_t)(e.rows * e.cols), cols = (uint32_t)e.cols;
+            const uint32_t np = (uint32_t)a.np;
+            const uint32_t e0 = (uint32_t)tile * (T * T) + (uint32_t)tid * 4u;
+#pragma unroll 1
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t idx = e0 + (uint32_t)k * 1024u;
+                if (idx >= nel) break;
+                const uint32_t xi = (np == cols) ? idx : (idx / cols) * np + idx % cols;
+                const uint2 ov = *reinterpret_cast<const uint2*>(O + xi);
+                float4 w = *reinterpret_cast<const float4*>(e.w + idx);
+                const float o[4] = {bf16_to_f32(ov.x & 0xffffu), bf16_to_f32(ov.x >> 16),
+                                    bf16_to_f32(ov.y & 0xffffu), bf16_to_f32(ov.y >> 16)};
+                apply4_serial(w, o, d, u);
+                *reinterpret_cast<float4*>(e.w + idx) = w;
+            }
+            continue;
+        }
+        const int64_t tiles_c = (e.cols + T - 1) / T;
+        const int64_t r0 = (tile / tiles_c) * T, c0 = (tile % tiles_c) * T;
+        const int64_t c = c0 + cg * 4;
+        if (e.trans) {
+            const int q = tid >> 2, seg = (tid & 3) * 16;
+            const int64_t orow = c0 + q;
+            const int64_t ocol = r0 + seg;
+            if (orow < e.cols && ocol < e.rows) {
+                const uint16_t* src = O + orow * a.np + ocol;
+                if (ocol + 16 <= e.rows) {
+                    uint4* d4 = reinterpret_cast<uint4*>(&tr[q][seg]);
+                    d4[0] = reinterpret_cast<const uint4*>(src)[0];
+                    d4[1] = reinterpret_cast<const uint4*>(src)[1];
+                } else {
+                    for (int k = 0; ocol + k < e.rows; ++k) tr[q][seg + k] = src[k];
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll 1
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = r0 + rg + 16 * i;
+            if (r >= e.rows || c >= e.cols) continue;
+            const int64_t base = r * e.cols + c;
+            const int nvalid = (int)((e.cols - c) < 4 ? (e.cols - c) : 4);
+            float o[4] = {0.f, 0.f, 0.f, 0.f};
+            if (e.trans) {
+                for (int j = 0; j < nvalid; ++j) o[j] = bf16_to_f32(tr[cg * 4 + j][rg + 16 * i]);
+            } else if (nvalid == 4 && (a.np & 3) == 0) {
+                const uint2 v = *reinterpret_cast<const uint2*>(O + r * a.np + c);
+                o[0] = bf16_to_f32(v.x & 0xffffu); o[1] = bf16_to_f32(v.x >> 16);
+                o[2] = bf16_to_f32(v.y & 0xffffu); o[3] = bf16_to_f32(v.y >> 16);
+            } else {
+                for (int j = 0; j < nvalid; ++j) o[j] = bf16_to_f32(O[r * a.np + c + j]);
+            }
+            if (vec && nvalid == 4) {
+                float4 w = *reinterpret_cast<const float4*>(e.w + base);
+                apply4_serial(w, o, d, u);
+                *reinterpret_cast<float4*>(e.w + base) = w;
+            } else {
+                for (int j = 0; j < nvalid; ++j) e.w[base + j] = apply_elem(e.w[base + j], o[j], d, u);
+            }
+        }
+        if (e.trans) __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // AdamW for the parameters that take it.  Each operation is one float64 rounding, in the
 // order below (contraction is off in this file); m and v are stored as float32.
 // ---------------------------------------------------------------------------------------
@@ -565,6 +919,30 @@ hipError_t launch_adamw(const AdamArgs& a, hipStream_t s) {
 hipError_t launch_apply(const ApplyArgs& a, hipStream_t s) {
     const unsigned grid = grid_for(a.total_tiles);
     hipLaunchKernelGGL(apply_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// One workgroup per CU for the side-stream kernels (see above).
+constexpr int64_t SIDE_GRID = 256;
+
+hipError_t launch_momentum_side(const MomentumArgs& a, int32_t grad_dtype, hipStream_t s) {
+    const unsigned grid = grid_for(a.total_tiles, SIDE_GRID);
+    if (grad_dtype == MUON_DTYPE_F32)
+        hipLaunchKernelGGL(momentum_side_kernel<MUON_DTYPE_F32>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(momentum_side_kernel<MUON_DTYPE_BF16>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize_side(const NormalizeArgs& a, hipStream_t s) {
+    const unsigned grid = grid_for((a.total_units + 255) / 256, SIDE_GRID);
+    hipLaunchKernelGGL(normalize_side_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply_side(const ApplyArgs& a, hipStream_t s) {
+    const unsigned grid = grid_for(a.total_tiles, SIDE_GRID);
+    hipLaunchKernelGGL(apply_side_kernel, dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -106,6 +106,10 @@ hipError_t launch_finalize(const FinalizeArgs& a, int64_t count, hipStream_t s);
 hipError_t launch_normalize(const NormalizeArgs& a, hipStream_t s);
 hipError_t launch_apply(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, hipStream_t s);
+// Side-stream variants (same results; sized to run beside the Newton–Schulz products).
+hipError_t launch_momentum_side(const MomentumArgs& a, int32_t grad_dtype, hipStream_t s);
+hipError_t launch_normalize_side(const NormalizeArgs& a, hipStream_t s);
+hipError_t launch_apply_side(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_small(const SmallNsArgs& a, int64_t total, hipStream_t s);
 

@@ -124,6 +124,8 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (scale_mode != MUON_SCALE_NONE && scale_mode != MUON_SCALE_ASPECT && scale_mode != MUON_SCALE_RMS_MATCH)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown scale_mode");
     const uint32_t flags = opts ? opts->flags : 0u;
+    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_DOUBLE_BUFFER)) != 0)
+        return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown flag bits");
 
     // ---- validate every descriptor -----------------------------------------------------
     std::vector<Interval> ivs;
@@ -259,20 +261,26 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
         total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 6 * WS_ALIGN;
     p->shared_regions = cap != 0 && total > cap;
     p->flags = flags;
+    const bool double_buffer = p->shared_regions && (flags & MUON_PLAN_DOUBLE_BUFFER) != 0;
 
     int32_t bucket_id = 0;
     for (const BucketGeo& g : geo) {
         int64_t per_chunk = (int64_t)g.members.size();
         if (p->shared_regions) {
+            // one region of up to `room` bytes, or two of up to `room` each (double buffering)
             const uint64_t pm = per_matrix_bytes(g.mp, g.np, g.ew);
-            const uint64_t room = cap > p->table_bytes + 6 * WS_ALIGN ? cap - p->table_bytes - 6 * WS_ALIGN : 0;
+            const uint64_t slack = (double_buffer ? 12 : 6) * WS_ALIGN;
+            uint64_t room = cap > p->table_bytes + slack ? cap - p->table_bytes - slack : 0;
+            if (double_buffer) room /= 2;
             const int64_t fit = (int64_t)(room / pm);
             if (fit < 1) {
                 delete p;
                 return set_error(MUON_ERR_WORKSPACE_TOO_SMALL,
                                  "one " + std::to_string(g.m) + "x" + std::to_string(g.n) +
-                                     " matrix needs " + std::to_string(pm + p->table_bytes + 6 * WS_ALIGN) +
-                                     " bytes of workspace; the cap is " + std::to_string(cap));
+                                     " matrix needs " +
+                                     std::to_string((double_buffer ? 2 : 1) * pm + p->table_bytes + slack) +
+                                     " bytes of workspace" + (double_buffer ? " with double buffering" : "") +
+                                     "; the cap is " + std::to_string(cap));
             }
             per_chunk = std::min(per_chunk, fit);
         }
@@ -315,7 +323,21 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
             off = c.region_off + c.region_bytes;
         }
     }
-    p->ws_bytes = p->shared_regions ? p->table_bytes + shared_max : off;
+    bool second = false;
+    if (double_buffer) {
+        // the tiled chunks alternate between two regions (the fused small-matrix chunks,
+        // which the two-stream pipeline runs one at a time first, stay in the first), so
+        // that consecutive tiled chunks never share one
+        int64_t k = 0;
+        for (Chunk& c : p->chunks) {
+            if (c.fused) continue;
+            if (k++ & 1) {
+                layout_region(c, p->table_bytes + shared_max);
+                second = true;
+            }
+        }
+    }
+    p->ws_bytes = p->shared_regions ? p->table_bytes + shared_max * (second ? 2 : 1) : off;
     if (p->ws_bytes == 0) p->ws_bytes = WS_ALIGN;
     *out = p;
     return MUON_OK;

@@ -105,6 +105,9 @@ struct muon_plan {
     uint64_t ws_given = 0;
     bool bound = false;
     muon::TimingState timing;
+    // the two-stream pipeline: a second stream and its ordering events, created at bind
+    void* side = nullptr;                 // hipStream_t
+    std::vector<void*> pipe_events;       // hipEvent_t, timing disabled
 };
 
 // An instantiated graph of one whole step.  It holds the device addresses of the

@@ -148,7 +148,8 @@ class Plan:
 
     @staticmethod
     def config(beta, lr, wd, a=wl.NS_A, b=wl.NS_B, c=wl.NS_C, steps=wl.NS_STEPS, eps=wl.NS_EPS,
-               coeffs=None, nesterov=False, dev_scalars: Optional[torch.Tensor] = None, adamw=None):
+               coeffs=None, nesterov=False, dev_scalars: Optional[torch.Tensor] = None, adamw=None,
+               pipeline=False):
         """A muon_step_config (and the host arrays it points to, which must stay alive)."""
         k = L.muon_step_config()
         k.beta, k.lr, k.wd, k.eps = beta, lr, wd, eps
@@ -161,6 +162,7 @@ class Plan:
             steps = len(flat) // 3
         k.steps = steps
         k.nesterov = 1 if nesterov else 0
+        k.pipeline = 1 if pipeline else 0
         if adamw is not None:
             keep = (keep, adamw)
             k.adamw = C.pointer(adamw)

@@ -365,3 +365,52 @@ def test_adamw_parameters_are_planned_by_role():
     k.lr, k.beta1, k.beta2, k.eps, k.wd, k.step = 1e-3, 0.9, 0.95, 1e-8, 0.1, 1
     assert L.muon_adamw_step(p, C.byref(k), None) == L.MUON_ERR_NOT_BOUND
     L.muon_plan_destroy(p)
+
+
+def test_double_buffered_regions_under_a_cap():
+    # tiled chunks alternate between two regions, each within half the remaining cap; the
+    # fused small chunks stay in the first; without a binding cap the flag changes nothing
+    shapes = [(1024, 4096)] * 40 + [(4096, 1024)] * 20 + [(64, 512)] * 5
+    st, p = _plan(_descs(shapes))
+    full = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(full))
+    plain = _infos(p)
+    L.muon_plan_destroy(p)
+    st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_DOUBLE_BUFFER)
+    assert st == 0 and _infos(p) == plain
+    L.muon_plan_destroy(p)
+    cap = full.value // 5
+    st, p = _plan(_descs(shapes), cap=cap, flags=L.MUON_PLAN_DOUBLE_BUFFER)
+    assert st == 0, L.muon_last_error()
+    nb = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(nb))
+    assert nb.value <= cap
+    infos = _infos(p)
+    tiled = [i for i in infos if not i["fused_small"]]
+    offs = [i["region_offset"] for i in tiled]
+    assert len(set(offs)) == 2 and all(offs[j] != offs[j - 1] for j in range(1, len(offs)))
+    lo, hi = sorted(set(offs))
+    assert all(i["region_offset"] == lo for i in infos if i["fused_small"])
+    # regions never overlap and end within the workspace
+    for i in infos:
+        end = i["region_offset"] + i["region_bytes"]
+        assert end <= nb.value
+        if i["region_offset"] == lo:
+            assert end <= hi
+    # about half the matrices per chunk of the single-region plan under the same cap
+    st1, p1 = _plan(_descs(shapes), cap=cap)
+    single = max(i["count"] for i in _infos(p1) if i["m"] == 1024)
+    double = max(i["count"] for i in tiled if i["m"] == 1024)
+    assert double <= (single + 1) // 2 + 1
+    L.muon_plan_destroy(p1)
+    L.muon_plan_destroy(p)
+    # too small for two matrices of the largest bucket
+    st, p = _plan(_descs([(4096, 4096)] * 2), cap=3 * 4096 * 4096 * 2 * 2,
+                  flags=L.MUON_PLAN_DOUBLE_BUFFER)
+    assert st == L.MUON_ERR_WORKSPACE_TOO_SMALL and b"double buffering" in L.muon_last_error()
+
+
+def test_unknown_plan_flags_are_refused():
+    st, p = _plan(_descs([(128, 256)]), flags=1 << 7)
+    assert st == L.MUON_ERR_INVALID_ARG and not p.value
+    assert b"flag" in L.muon_last_error()
