@@ -152,7 +152,7 @@ def main(argv=None):
         if need > free - (4 << 30):
             cap = 8 << 30
     plan = harness.Plan(params, max_workspace_bytes=cap,
-                        flags=L.MUON_PLAN_DOUBLE_BUFFER if (cap and args.pipeline) else 0)
+                        flags=L.MUON_PLAN_PIPELINE if args.pipeline else 0)
     stream = torch.cuda.current_stream()
     kw = dict(a=w.a, b=w.b, c=w.c, steps=w.steps, eps=w.eps, adamw=adamw_cfg)
 

@@ -127,13 +127,15 @@ typedef struct muon_plan_opts {
 /* Orthogonalise small matrices with the tiled kernels too, instead of the fused
  * whole-iteration kernel (both give bitwise the same result; this exists to show it). */
 #define MUON_PLAN_TILED_SMALL 1u
-/* With a workspace cap that splits buckets into chunks: lay the chunks out in two regions
- * of at most half the remaining cap each, alternating between consecutive tiled chunks,
- * so that the two-stream pipeline (muon_step_config.pipeline) can prepare one chunk while
- * the previous one is orthogonalised.  Chunks hold about half as many matrices.  No
- * effect without a cap, or when everything fits under it (every chunk then has its own
- * region). */
-#define MUON_PLAN_DOUBLE_BUFFER 2u
+/* Plan for the two-stream step (muon_step_config.pipeline), which hides one chunk's
+ * neighbours' elementwise work behind its Newton–Schulz products and so needs several
+ * chunks: a large bucket is split into up to 8 chunks, as many as keep at least 2048
+ * SYRK workgroups per launch (the chunk sizes of one bucket differ by at most one).
+ * With a workspace cap that splits buckets anyway, the chunks are laid out in two
+ * regions of at most half the remaining cap each, alternating between consecutive tiled
+ * chunks, so that one chunk can be prepared while the previous one is orthogonalised.
+ * Results do not depend on the chunking. */
+#define MUON_PLAN_PIPELINE 2u
 
 typedef struct muon_plan muon_plan;
 
@@ -304,7 +306,7 @@ typedef struct muon_step_config {
      * Microsoft AI", method details section 5, "Scaling Muon to 16K GPUs").  Results are
      * bitwise those of 0.  It needs at least two tiled chunks, no two consecutive ones
      * in one workspace region (always so without a binding cap; with one, plan with
-     * MUON_PLAN_DOUBLE_BUFFER); otherwise the step runs as with 0.  Steps of one plan
+     * MUON_PLAN_PIPELINE); otherwise the step runs as with 0.  Steps of one plan
      * must not overlap: the second stream is shared by every call on the plan. */
     int32_t pipeline;
 } muon_step_config;

@@ -52,7 +52,7 @@ MUON_OPT_ADAMW = 1
 MUON_OPT_NONE = 2
 
 MUON_PLAN_TILED_SMALL = 1
-MUON_PLAN_DOUBLE_BUFFER = 2
+MUON_PLAN_PIPELINE = 2
 
 MUON_SCALE_NONE = 0
 MUON_SCALE_ASPECT = 1

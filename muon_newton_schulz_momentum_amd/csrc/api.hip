@@ -358,36 +358,53 @@ std::vector<int32_t> pipeline_chunks(const muon_plan* p) {
     std::vector<int32_t> t;
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
         if (!p->chunks[(size_t)i].fused) t.push_back(i);
-    if (t.size() < 2 || !p->side || p->pipe_events.size() < 2 + 2 * t.size()) return {};
+    if (t.size() < 2 || !p->side || p->pipe_events.size() < 1 + 4 * t.size()) return {};
     for (size_t j = 1; j < t.size(); ++j)
         if (p->chunks[(size_t)t[j]].region_off == p->chunks[(size_t)t[j - 1]].region_off) return {};
     return t;
 }
 
+// Estimates for placing work on the side stream: the products' algorithmic rate is taken
+// above what they reach and the side kernels' bandwidth below, so that a window is never
+// overestimated and side work does not outlast the products it hides behind.
+constexpr double EST_NS_FLOPS = 1.2e15;     // FLOP/s
+constexpr double EST_SIDE_BW = 1.5e12;      // B/s
+double est_ns_s(const Chunk& c, int32_t steps) { return steps * ns_iter_flops(c) / EST_NS_FLOPS; }
+double est_prep_s(const Chunk& c) {         // momentum + normalise bytes, side kernels
+    const double el = (double)c.count * c.m * c.n;
+    return el * ((c.grad_dtype == MUON_DTYPE_F32 ? 14.0 : 12.0) + 4.0) / EST_SIDE_BW;
+}
+double est_apply_s(const Chunk& c) { return (double)c.count * c.m * c.n * 10.0 / EST_SIDE_BW; }
+
 // The whole step with two streams.  The pages overlap the exchange of the next batch of
 // matrices with the orthogonalisation of the current one ("Frontier Pre-training at
 // Microsoft AI", method details section 5, "Scaling Muon to 16K GPUs", the prefetching of
 // the next batch).  On one GPU the work beside the products is the HBM-bound part of the
-// step: chunk j+1's momentum and normaliser and chunk j-1's apply run on the plan's side
-// stream while chunk j's Newton–Schulz products run on the caller's stream, in the
-// side-stream kernels sized to share each compute unit with a product workgroup.
+// step: while chunk j's Newton–Schulz products run on the caller's stream s, chunk j+1's
+// momentum and normaliser (P_{j+1}) and chunk j-1's apply (A_{j-1}) run on the plan's side
+// stream d, in the side-stream kernels sized to share each compute unit with a product
+// workgroup.  A task goes to d only if it fits the window (estimates above: side kernels
+// are slower than the full-speed ones); otherwise it runs at full speed on s, P_{j+1} after
+// NS(u_j) and A_{j-1} before it, so that the step is never much slower than one stream.
 //
-// Order, for the tiled chunks u_0 .. u_{T-1} (small fused chunks first, as in the
-// one-stream order, on the caller's stream s):
-//   s: momentum(u_0), prep(u_0), [fork], NS(u_0), [wait prep(u_1)], NS(u_1), ...,
-//      NS(u_{T-1}), apply(u_{T-1}), [join]
-//   d: momentum(u_1), prep(u_1), [wait NS(u_0)], apply(u_0), momentum(u_2), prep(u_2),
-//      [wait NS(u_1)], apply(u_1), ...
-// Consecutive tiled chunks are in different regions, so what runs side by side never
-// touches the same workspace bytes; u_{j+1}'s momentum runs after u_{j-1}'s apply on d,
-// so two regions are enough.  Events: 0 fork, 1 join, 2 + j prep(u_j) done, 2 + T + j
-// NS(u_j) done.
+// For the tiled chunks u_0 .. u_{T-1} (small fused chunks first, as in the one-stream
+// order, on s), with every task on d:
+//   s: P_0, [W_0], NS(u_0), [wait P_1], [W_1], NS(u_1), ..., NS(u_{T-1}), A_{T-1}, [join]
+//   d: [wait W_0], P_1, [wait NS(u_0)], A_0, [wait W_1], P_2, [wait NS(u_1)], A_1, ...
+// W_j marks the start of window j on s: P_{j+1} waits for it, so it never starts before
+// NS(u_{j-1}) and an A_{j-1} run on s are done; a P_{j+1} run on s after an A_{j-1} run on
+// d waits for that apply when the two chunks share a region.  Consecutive tiled chunks
+// are in different regions, so what runs side by side never touches the same workspace
+// bytes, and two regions are enough.  Events: 0 join, 1 + j W_j, 1 + T + j P_j done,
+// 1 + 2T + j NS(u_j) done, 1 + 3T + j A_j done.
 muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, const StepCfg& cfg, hipStream_t s) {
     muon_status st;
     hipError_t e = hipSuccess;
     const float* abc = cfg.abc.data();
     const size_t T = u.size();
     hipStream_t d = (hipStream_t)p->side;
+    auto ch = [&](size_t j) -> const Chunk& { return p->chunks[(size_t)u[j]]; };
+    const size_t EV_JOIN = 0, EV_W = 1, EV_P = 1 + T, EV_NS = 1 + 2 * T, EV_A = 1 + 3 * T;
 
     std::vector<int32_t> small;
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
@@ -400,33 +417,64 @@ muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, co
             if ((st = apply_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
     } else {
         for (int32_t i : small) {
-            const Chunk& ch = p->chunks[(size_t)i];
-            if ((st = momentum_chunk(p, ch, cfg, s)) != MUON_OK) return st;
+            const Chunk& c = p->chunks[(size_t)i];
+            if ((st = momentum_chunk(p, c, cfg, s)) != MUON_OK) return st;
             if ((st = ns_one(p, i, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
-            if ((st = apply_chunk(p, ch, cfg, s)) != MUON_OK) return st;
+            if ((st = apply_chunk(p, c, cfg, s)) != MUON_OK) return st;
         }
     }
 
-    const Chunk& c0 = p->chunks[(size_t)u[0]];
+    // placement: window j (NS(u_j)) takes P_{j+1} and A_{j-1} if both fit, else whichever
+    // of the two fits (P first: an exposed P holds up the next window), else neither
+    std::vector<char> p_side(T, 0), a_side(T, 0);
+    for (size_t j = 0; j < T; ++j) {
+        const double win = est_ns_s(ch(j), cfg.steps);
+        const double tp = j + 1 < T ? est_prep_s(ch(j + 1)) : 0.0;
+        const double ta = j > 0 ? est_apply_s(ch(j - 1)) : 0.0;
+        const bool has_p = j + 1 < T, has_a = j > 0;
+        if (has_p && has_a && tp + ta <= win) {
+            p_side[j + 1] = a_side[j - 1] = 1;
+        } else {
+            if (has_p && tp <= win) p_side[j + 1] = 1;
+            else if (has_a && ta <= win) a_side[j - 1] = 1;
+        }
+    }
+
+    const Chunk& c0 = ch(0);
     if ((st = momentum_chunk(p, c0, cfg, s)) != MUON_OK) return st;
     if ((st = ns_prep(p, c0, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
-    if ((e = record(p, 0, s)) != hipSuccess || (e = wait(p, 0, d)) != hipSuccess)
-        return hip_fail(e, "pipeline fork");
     for (size_t j = 0; j < T; ++j) {
-        const Chunk& cj = p->chunks[(size_t)u[j]];
-        if (j > 0 && (e = wait(p, 2 + j, s)) != hipSuccess) return hip_fail(e, "pipeline wait");
+        const Chunk& cj = ch(j);
+        if (j > 0 && p_side[j] && (e = wait(p, EV_P + j, s)) != hipSuccess) return hip_fail(e, "pipeline wait");
+        if (j > 0 && !a_side[j - 1] && (st = apply_chunk(p, ch(j - 1), cfg, s)) != MUON_OK) return st;
+        if ((e = record(p, EV_W + j, s)) != hipSuccess) return hip_fail(e, "pipeline record");
+        if (j == 0 && (e = wait(p, EV_W, d)) != hipSuccess) return hip_fail(e, "pipeline fork");
         if ((st = ns_iterate(p, cj, abc, cfg.steps, s)) != MUON_OK) return st;
-        if (j + 1 == T) break;
-        if ((e = record(p, 2 + T + j, s)) != hipSuccess) return hip_fail(e, "pipeline record");
-        const Chunk& cn = p->chunks[(size_t)u[j + 1]];
-        if ((st = momentum_chunk(p, cn, cfg, d, true)) != MUON_OK) return st;
-        if ((st = ns_prep(p, cn, cfg.steps, cfg.eps, d, true)) != MUON_OK) return st;
-        if ((e = record(p, 2 + j + 1, d)) != hipSuccess || (e = wait(p, 2 + T + j, d)) != hipSuccess)
-            return hip_fail(e, "pipeline record");
-        if ((st = apply_chunk(p, cj, cfg, d, true)) != MUON_OK) return st;
+        if (j + 1 < T) {
+            const Chunk& cn = ch(j + 1);
+            if (p_side[j + 1]) {
+                if ((e = wait(p, EV_W + j, d)) != hipSuccess) return hip_fail(e, "pipeline wait");
+                if ((st = momentum_chunk(p, cn, cfg, d, true)) != MUON_OK) return st;
+                if ((st = ns_prep(p, cn, cfg.steps, cfg.eps, d, true)) != MUON_OK) return st;
+                if ((e = record(p, EV_P + j + 1, d)) != hipSuccess) return hip_fail(e, "pipeline record");
+            } else {
+                if (j > 0 && a_side[j - 1] && cn.region_off == ch(j - 1).region_off &&
+                    (e = wait(p, EV_A + j - 1, s)) != hipSuccess)
+                    return hip_fail(e, "pipeline wait");
+                if ((st = momentum_chunk(p, cn, cfg, s)) != MUON_OK) return st;
+                if ((st = ns_prep(p, cn, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+            }
+        }
+        if (a_side[j]) {
+            if ((e = record(p, EV_NS + j, s)) != hipSuccess || (e = wait(p, EV_NS + j, d)) != hipSuccess)
+                return hip_fail(e, "pipeline record");
+            if ((st = apply_chunk(p, cj, cfg, d, true)) != MUON_OK) return st;
+            if ((e = record(p, EV_A + j, d)) != hipSuccess) return hip_fail(e, "pipeline record");
+        }
     }
-    if ((st = apply_chunk(p, p->chunks[(size_t)u[T - 1]], cfg, s)) != MUON_OK) return st;
-    if ((e = record(p, 1, d)) != hipSuccess || (e = wait(p, 1, s)) != hipSuccess) return hip_fail(e, "pipeline join");
+    if ((st = apply_chunk(p, ch(T - 1), cfg, s)) != MUON_OK) return st;
+    if ((e = record(p, EV_JOIN, d)) != hipSuccess || (e = wait(p, EV_JOIN, s)) != hipSuccess)
+        return hip_fail(e, "pipeline join");
     return cfg.adam ? adam_run(p, cfg.adam_args, s) : MUON_OK;
 }
 
@@ -561,7 +609,7 @@ muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream)
         if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipStreamCreateWithFlags");
         p->side = side;
     }
-    while (p->pipe_events.size() < 2 + 2 * p->chunks.size()) {
+    while (p->pipe_events.size() < 1 + 4 * p->chunks.size()) {
         hipEvent_t ev = nullptr;
         e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
         if (e != hipSuccess) return hip_fail(e, "muon_plan_bind: hipEventCreateWithFlags");

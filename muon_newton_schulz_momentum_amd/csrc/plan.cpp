@@ -124,7 +124,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (scale_mode != MUON_SCALE_NONE && scale_mode != MUON_SCALE_ASPECT && scale_mode != MUON_SCALE_RMS_MATCH)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown scale_mode");
     const uint32_t flags = opts ? opts->flags : 0u;
-    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_DOUBLE_BUFFER)) != 0)
+    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_PIPELINE)) != 0)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown flag bits");
 
     // ---- validate every descriptor -----------------------------------------------------
@@ -261,11 +261,23 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
         total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 6 * WS_ALIGN;
     p->shared_regions = cap != 0 && total > cap;
     p->flags = flags;
-    const bool double_buffer = p->shared_regions && (flags & MUON_PLAN_DOUBLE_BUFFER) != 0;
+    const bool pipeline = (flags & MUON_PLAN_PIPELINE) != 0;
+    const bool double_buffer = p->shared_regions && pipeline;
 
     int32_t bucket_id = 0;
     for (const BucketGeo& g : geo) {
         int64_t per_chunk = (int64_t)g.members.size();
+        const bool fused = !(flags & MUON_PLAN_TILED_SMALL) && g.mp == 64 && g.np <= SMALL_NS_MAX_N;
+        if (pipeline && !fused) {
+            // The two-stream step hides a chunk's neighbours' elementwise work behind its
+            // products, which needs several chunks per large bucket: up to PIPE_MAX_SPLIT,
+            // each keeping at least PIPE_MIN_WG SYRK workgroups (the smallest product
+            // launch), so that every launch still fills the chip many times over.
+            const int64_t tm = g.mp / g.tile, tri = tm * (tm + 1) / 2;
+            const int64_t n_min = ceil_div(PIPE_MIN_WG, tri);
+            const int64_t k = std::max<int64_t>(1, std::min<int64_t>(PIPE_MAX_SPLIT, per_chunk / n_min));
+            per_chunk = ceil_div(per_chunk, k);
+        }
         if (p->shared_regions) {
             // one region of up to `room` bytes, or two of up to `room` each (double buffering)
             const uint64_t pm = per_matrix_bytes(g.mp, g.np, g.ew);
@@ -293,7 +305,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
             Chunk ch{};
             ch.bucket = bucket_id; ch.grad_dtype = g.gdt;
             ch.m = g.m; ch.n = g.n; ch.mp = g.mp; ch.np = g.np; ch.tile = g.tile;
-            ch.fused = !(flags & MUON_PLAN_TILED_SMALL) && g.mp == 64 && g.np <= SMALL_NS_MAX_N;
+            ch.fused = fused;
             ch.count = cnt; ch.first = (int64_t)p->table.size(); ch.ew_tiles = g.ew;
             ch.off_table = (uint64_t)ch.first * sizeof(MatEntry);
             const int32_t cidx = (int32_t)p->chunks.size();
@@ -326,8 +338,8 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     bool second = false;
     if (double_buffer) {
         // the tiled chunks alternate between two regions (the fused small-matrix chunks,
-        // which the two-stream pipeline runs one at a time first, stay in the first), so
-        // that consecutive tiled chunks never share one
+        // which the two-stream step runs one at a time first, stay in the first), so that
+        // consecutive tiled chunks never share one
         int64_t k = 0;
         for (Chunk& c : p->chunks) {
             if (c.fused) continue;

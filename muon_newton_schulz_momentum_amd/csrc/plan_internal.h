@@ -128,6 +128,10 @@ void clear_error();
 constexpr int EW_TILE = 64;          // elementwise tile edge
 constexpr int SMALL_NS_MAX_N = 1024; // widest padded n of the fused small-matrix kernel
 constexpr uint64_t WS_ALIGN = 256;   // workspace sub-buffer alignment
+// MUON_PLAN_PIPELINE chunking: at most this many chunks per bucket, each with at least this
+// many SYRK workgroups
+constexpr int64_t PIPE_MAX_SPLIT = 8;
+constexpr int64_t PIPE_MIN_WG = 2048;
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

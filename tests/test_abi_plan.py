@@ -367,20 +367,38 @@ def test_adamw_parameters_are_planned_by_role():
     L.muon_plan_destroy(p)
 
 
+def test_pipeline_plans_split_large_buckets():
+    # up to 8 chunks per bucket, each with at least 2048 SYRK workgroups (upper-triangle
+    # tiles of 256 x 256: 10 for m = 1024, 36 for m = 2048, 595 for m = 8704)
+    cases = [((1024, 4096), 1536, 7), ((2048, 2048), 96, 1), ((2048, 2048), 200, 3), ((8704, 8704), 4, 1),
+             ((2048, 2048), 5000, 8), ((64, 512), 3000, 1)]
+    for shape, count, want in cases:
+        for flags, expect in ((0, 1), (L.MUON_PLAN_PIPELINE, want)):
+            st, p = _plan(_descs([shape] * count), flags=flags)
+            assert st == 0, L.muon_last_error()
+            infos = _infos(p)
+            assert len(infos) == expect, (shape, count, flags, len(infos))
+            sizes = [i["count"] for i in infos]
+            assert sum(sizes) == count and max(sizes) - min(sizes) <= 1
+            assert all(i["shared_region"] == 0 for i in infos)
+            L.muon_plan_destroy(p)
+
+
 def test_double_buffered_regions_under_a_cap():
     # tiled chunks alternate between two regions, each within half the remaining cap; the
-    # fused small chunks stay in the first; without a binding cap the flag changes nothing
+    # fused small chunks stay in the first; without a binding cap (and buckets too small to
+    # split) the flag changes nothing
     shapes = [(1024, 4096)] * 40 + [(4096, 1024)] * 20 + [(64, 512)] * 5
     st, p = _plan(_descs(shapes))
     full = C.c_uint64()
     L.muon_plan_workspace_bytes(p, C.byref(full))
     plain = _infos(p)
     L.muon_plan_destroy(p)
-    st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_DOUBLE_BUFFER)
+    st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_PIPELINE)
     assert st == 0 and _infos(p) == plain
     L.muon_plan_destroy(p)
     cap = full.value // 5
-    st, p = _plan(_descs(shapes), cap=cap, flags=L.MUON_PLAN_DOUBLE_BUFFER)
+    st, p = _plan(_descs(shapes), cap=cap, flags=L.MUON_PLAN_PIPELINE)
     assert st == 0, L.muon_last_error()
     nb = C.c_uint64()
     L.muon_plan_workspace_bytes(p, C.byref(nb))
@@ -406,7 +424,7 @@ def test_double_buffered_regions_under_a_cap():
     L.muon_plan_destroy(p)
     # too small for two matrices of the largest bucket
     st, p = _plan(_descs([(4096, 4096)] * 2), cap=3 * 4096 * 4096 * 2 * 2,
-                  flags=L.MUON_PLAN_DOUBLE_BUFFER)
+                  flags=L.MUON_PLAN_PIPELINE)
     assert st == L.MUON_ERR_WORKSPACE_TOO_SMALL and b"double buffering" in L.muon_last_error()
 
 

@@ -132,7 +132,7 @@ def test_pipeline_with_double_buffered_workspace_cap():
     free = harness.Plan(_clone(ps), bind=False)
     cap = free.workspace_bytes // 3
     free.close()
-    plan = harness.Plan(ps, max_workspace_bytes=cap, flags=L.MUON_PLAN_DOUBLE_BUFFER)
+    plan = harness.Plan(ps, max_workspace_bytes=cap, flags=L.MUON_PLAN_PIPELINE)
     ref = harness.Plan(ref_ps)                  # no cap: its own chunking, same per-matrix math
     assert plan.workspace_bytes <= cap
     tiled = _tiled_chunks(plan)
@@ -189,5 +189,35 @@ def test_pipeline_with_adamw_params():
         assert torch.equal(_bits(x.weight), _bits(y.weight)), ("W", i)
         assert torch.equal(_bits(x.momentum), _bits(y.momentum)), ("M", i)
     assert torch.equal(_bits(ps[8].exp_avg_sq), _bits(ref_ps[8].exp_avg_sq))
+    plan.close()
+    ref.close()
+
+
+def test_pipeline_plan_splits_a_large_bucket_and_places_by_window():
+    # a large expert-like bucket (split into two chunks by MUON_PLAN_PIPELINE) and a
+    # one-matrix router chunk: the router's window is far too short to hide the experts'
+    # apply, which then runs at full speed on the caller's stream; bits as one stream
+    from muon_newton_schulz_momentum_amd import binding as L, harness
+    shapes = [((1024, 1536), "f32")] * 420 + [((512, 1536), "f32")]
+    ps = _params(shapes, seed=740)
+    ref_ps = _clone(ps)
+    plan = harness.Plan(ps, flags=L.MUON_PLAN_PIPELINE)
+    ref = harness.Plan(ref_ps)
+    assert plan.n_chunks == 3 and ref.n_chunks == 2
+    anchor = 0
+    snap = _snap(ps[anchor])
+    for step in range(2):
+        plan.step_ex(BETA, LR, WD, pipeline=True)
+        ref.step_ex(BETA, LR, WD)
+        torch.cuda.synchronize()
+        _same(ps, ref_ps, plan, ref, f"split step {step}")
+        if step == 0:
+            _oracle_anchor(snap, plan, ps, anchor)
+    g = plan.capture_ex(BETA, LR, WD, pipeline=True)
+    g.launch()
+    ref.step_ex(BETA, LR, WD)
+    torch.cuda.synchronize()
+    _same(ps, ref_ps, plan, ref, "split replay")
+    g.close()
     plan.close()
     ref.close()
