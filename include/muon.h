@@ -359,7 +359,11 @@ MUON_API void muon_graph_destroy(muon_graph* graph);
 #define MUON_KERNEL_APPLY 6
 #define MUON_KERNEL_NS_SMALL 7
 #define MUON_KERNEL_ADAMW 8
-#define MUON_KERNEL_COUNT 9
+/* the side-stream kernels of the two-stream step (muon_step_config.pipeline) */
+#define MUON_KERNEL_MOMENTUM_SIDE 9
+#define MUON_KERNEL_NORMALIZE_SIDE 10
+#define MUON_KERNEL_APPLY_SIDE 11
+#define MUON_KERNEL_COUNT 12
 
 /* Start recording a HIP event pair around every kernel launch of this plan (up to
  * `capacity` launches; later ones go unrecorded).  capacity = 0 stops recording.

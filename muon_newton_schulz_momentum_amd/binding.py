@@ -45,7 +45,10 @@ MUON_KERNEL_GEMM_AXPY = 5
 MUON_KERNEL_APPLY = 6
 MUON_KERNEL_NS_SMALL = 7
 MUON_KERNEL_ADAMW = 8
-MUON_KERNEL_COUNT = 9
+MUON_KERNEL_MOMENTUM_SIDE = 9
+MUON_KERNEL_NORMALIZE_SIDE = 10
+MUON_KERNEL_APPLY_SIDE = 11
+MUON_KERNEL_COUNT = 12
 
 MUON_OPT_DEFAULT = 0
 MUON_OPT_ADAMW = 1

@@ -152,9 +152,9 @@ muon_status momentum_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cf
     a.dev_scalars = cfg.dev;
     a.nesterov = cfg.nesterov ? 1 : 0;
     const double gsz = c.grad_dtype == MUON_DTYPE_F32 ? 4.0 : 2.0;
-    TimedLaunch tl(p, MUON_KERNEL_MOMENTUM, (double)c.count * c.m * c.n * (10.0 + gsz), s);
-    const hipError_t e = (side && side_ok(c)) ? launch_momentum_side(a, c.grad_dtype, s)
-                                              : launch_momentum(a, c.grad_dtype, s);
+    const bool sk = side && side_ok(c);
+    TimedLaunch tl(p, sk ? MUON_KERNEL_MOMENTUM_SIDE : MUON_KERNEL_MOMENTUM, (double)c.count * c.m * c.n * (10.0 + gsz), s);
+    const hipError_t e = sk ? launch_momentum_side(a, c.grad_dtype, s) : launch_momentum(a, c.grad_dtype, s);
     tl.done(s);
     return e == hipSuccess ? MUON_OK : hip_fail(e, "momentum kernel launch");
 }
@@ -181,7 +181,7 @@ muon_status ns_prep(const muon_plan* p, const Chunk& c, int32_t steps, float eps
     }
     {
         NormalizeArgs n{xq, ns_start(p, c, steps), inv, c.m, c.n, c.mp, c.np, c.count * c.mp * c.np / 8};
-        TimedLaunch tl(p, MUON_KERNEL_NORMALIZE, (double)c.count * c.m * c.n * 4.0, s);
+        TimedLaunch tl(p, side ? MUON_KERNEL_NORMALIZE_SIDE : MUON_KERNEL_NORMALIZE, (double)c.count * c.m * c.n * 4.0, s);
         e = side ? launch_normalize_side(n, s) : launch_normalize(n, s);
         tl.done(s);
         if (e != hipSuccess) return hip_fail(e, "normalize kernel launch");
@@ -339,8 +339,9 @@ muon_status apply_chunk(const muon_plan* p, const Chunk& c, const StepCfg& cfg, 
     a.d = 1.0 - lw;                                       // one float64 rounding
     a.lr = cfg.lr;
     a.dev_scalars = cfg.dev;
-    TimedLaunch tl(p, MUON_KERNEL_APPLY, (double)c.count * c.m * c.n * 10.0, s);
-    const hipError_t e = (side && side_ok(c)) ? launch_apply_side(a, s) : launch_apply(a, s);
+    const bool sk = side && side_ok(c);
+    TimedLaunch tl(p, sk ? MUON_KERNEL_APPLY_SIDE : MUON_KERNEL_APPLY, (double)c.count * c.m * c.n * 10.0, s);
+    const hipError_t e = sk ? launch_apply_side(a, s) : launch_apply(a, s);
     tl.done(s);
     return e == hipSuccess ? MUON_OK : hip_fail(e, "apply kernel launch");
 }
@@ -854,6 +855,9 @@ const char* muon_kernel_name(int32_t k) {
         case MUON_KERNEL_APPLY: return "apply";
         case MUON_KERNEL_NS_SMALL: return "ns_small";
         case MUON_KERNEL_ADAMW: return "adamw";
+        case MUON_KERNEL_MOMENTUM_SIDE: return "momentum_side";
+        case MUON_KERNEL_NORMALIZE_SIDE: return "normalize_side";
+        case MUON_KERNEL_APPLY_SIDE: return "apply_side";
         default: return "unknown";
     }
 }
