@@ -501,11 +501,15 @@ void ns_vs_kernel(NsArgs p) {
     static_assert(SMEM >= TILE * TILE * 2, "epilogue tile fits");
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-  // one tile per workgroup, or (PERSIST) the workgroup's tiles one after another
+  // one tile per workgroup, or (PERSIST) the workgroup's tiles one after another; in the
+  // persistent case the next tile's first K step is fetched into the staging registers
+  // before the current tile's epilogue (see below)
+  i32x4 sa[NCH], sb[NCH];
+  int b_next = -1;
   for (int it = 0;; ++it) {
     int b;
     if (PERSIST) {
-        b = persistent_tile(blockIdx.x, gridDim.x, it, p.total_tiles);
+        b = it == 0 ? persistent_tile(blockIdx.x, gridDim.x, 0, p.total_tiles) : b_next;
         if (b < 0) break;
         if (it > 0) __syncthreads();                      // the last tile's LDS reads are done
     } else {
@@ -548,7 +552,10 @@ void ns_vs_kernel(NsArgs p) {
         w_kn[par] = OFF_B + klo * TILE * 2 + (((((nc >> 2) ^ (swz % KN_NG)) << 2) | (nc & 3)) << 4);
     }
 
-    i32x4 sa[NCH], sb[NCH];
+    // K step 0 already in sa / sb (the axpy only: in the symmetric products the extra live
+    // registers would cost the side-stream kernels their room on the CU)
+    constexpr bool PF = PERSIST && MODE == NS_AXPY;
+    const bool prefetched = PF && it > 0;
     auto gload_a = [&](int i, int kt) {
         sa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, va, kt * BK * 2 + i * RP_ROWS * p.lda * 2, 0);
     };
@@ -620,11 +627,14 @@ void ns_vs_kernel(NsArgs p) {
     // The main loop is straight-line code: every condition below is a compile-time
     // constant (diagonal tile or not, last two K steps or not), so the compiler's wait
     // counts stay exact (a branch would make it wait for every outstanding load).
-    auto run = [&](auto diag_c) {
-        constexpr bool DG = decltype(diag_c)::value;
-        // prologue: K step 0 into stage 0, K step 1 into the staging registers
+    auto run = [&](auto diag_c, auto pre_c) {
+        constexpr bool DG = decltype(diag_c)::value, PRE = decltype(pre_c)::value;
+        // prologue: K step 0 into stage 0 (already in the staging registers when PRE),
+        // K step 1 into the staging registers
+        if (!PRE) {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) { gload_a(i, 0); if (!DG) gload_b(i, 0); }
+            for (int i = 0; i < NCH; ++i) { gload_a(i, 0); if (!DG) gload_b(i, 0); }
+        }
 #pragma unroll
         for (int i = 0; i < NCH; ++i) { swrite_a(i, 0); if (!DG) swrite_b(i, 0); }
 #pragma unroll
@@ -677,8 +687,16 @@ void ns_vs_kernel(NsArgs p) {
         kstep(ic<0>{}, yes, no, nk - 2);
         kstep(ic<1>{}, no, no, nk - 1);
     };
-    if (diag) run(std::true_type{});
-    else run(std::false_type{});
+    // separate code for prefetched tiles, so that the compiler's wait before the first
+    // staging write counts the previous epilogue's stores instead of merging with the
+    // fresh-load path
+    if (prefetched) {
+        if (diag) run(std::true_type{}, std::true_type{});
+        else run(std::false_type{}, std::true_type{});
+    } else {
+        if (diag) run(std::true_type{}, std::false_type{});
+        else run(std::false_type{}, std::false_type{});
+    }
     // ---- epilogue ---------------------------------------------------------------------
     // The MFMAs take the right operand first, so each 32 x 32 block is accumulated
     // transposed: acc[i][j][4q + w] = D[wm0 + 32i + (lane & 31)][wn0 + 32j + 8q + 4(lane >> 5) + w],
@@ -726,6 +744,39 @@ void ns_vs_kernel(NsArgs p) {
             }
         }
     }
+    if (PERSIST) b_next = persistent_tile(blockIdx.x, gridDim.x, it + 1, p.total_tiles);
+    if (PF) {
+        // The next tile's K step 0 goes out now, after the combine (so that it does not add
+        // to the epilogue's register peak) and ahead of this tile's stores: the
+        // vector-memory counter retires in issue order and counts stores too, so the next
+        // prologue then waits only for these loads, not for the stores to drain.
+        // the staging registers' old contents are dead on every path from here (otherwise
+        // they would stay live through the epilogue into the next iteration)
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            sa[i] = __builtin_nondeterministic_value(sa[i]);
+            sb[i] = __builtin_nondeterministic_value(sb[i]);
+        }
+        if (b_next >= 0) {
+            const int nmat = b_next / p.tiles_per_mat, nt = b_next - nmat * p.tiles_per_mat;
+            int nti, ntj;
+            if (MODE == NS_AXPY) grid_decode(nt, p.tiles_m, p.tiles_n, nti, ntj);
+            else tri_decode(nt, p.tiles_m, nti, ntj);
+            const int64_t na0 = (int64_t)nti * TILE * p.lda;
+            const __amdgpu_buffer_rsrc_t nra = make_rsrc(p.opa + (int64_t)nmat * p.stride_a + na0, p.stride_a - na0);
+            const int64_t nb0 = (MODE == NS_AXPY) ? (int64_t)ntj * TILE : (int64_t)ntj * TILE * p.ldb;
+            const __amdgpu_buffer_rsrc_t nrb = make_rsrc(p.opb + (int64_t)nmat * p.stride_b + nb0, p.stride_b - nb0);
+            const bool ndiag = MODE != NS_AXPY && nti == ntj;
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                sa[i] = __builtin_amdgcn_raw_buffer_load_b128(nra, va, i * RP_ROWS * p.lda * 2, 0);
+                if (MODE == NS_AXPY)
+                    sb[i] = __builtin_amdgcn_raw_buffer_load_b128(nrb, vb_kn, KN_ROWS * i * p.ldb * 2, 0);
+                else if (!ndiag)
+                    sb[i] = __builtin_amdgcn_raw_buffer_load_b128(nrb, vb_rp, i * RP_ROWS * p.ldb * 2, 0);
+            }
+        }
+    }
     if (MODE == NS_POLY || MODE == NS_AXPY) lds_wait_barrier();   // E reads done before T is written
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -737,7 +788,7 @@ void ns_vs_kernel(NsArgs p) {
     lds_wait_barrier();
     // the tile: 256 rows x 32 granules, whole rows per 32 lanes
     uint16_t* orow = out + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
-#pragma unroll 4
+#pragma unroll
     for (int s2 = 0; s2 < TILE * 32 / NT; ++s2) {
         const int gi = tid + NT * s2;
         const int r = gi >> 5, g = gi & 31;
@@ -752,7 +803,8 @@ void ns_vs_kernel(NsArgs p) {
         const int x = lane & 15, grp = lane >> 4;
         const int ax = x & 3, mx = x >> 2;
 #pragma unroll 2
-        for (int u = wave; u < 128; u += NW) {            // 16 columns x 32 rows per unit
+        for (int u0 = 0; u0 < 128; u0 += NW) {            // 16 columns x 32 rows per unit
+            const int u = u0 + wave;
             const int c0 = (u & 15) * 16, r0 = (u >> 4) * 32 + 8 * grp;
             const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(T + tb(r0 + mx, c0 + 4 * ax)));
             const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(T + tb(r0 + 4 + mx, c0 + 4 * ax)));
