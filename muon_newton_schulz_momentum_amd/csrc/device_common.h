@@ -8,15 +8,22 @@
 namespace muon {
 namespace dev {
 
-// float32 -> bfloat16 bits, round to nearest, ties to even.  Adding 0x7FFF plus the
-// lowest kept bit to the 32-bit pattern carries into the kept half exactly when the
-// dropped half is above the midpoint, or at it with an odd kept half.  NaNs stay NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// float32 -> bfloat16 bits, round to nearest, ties to even, by gfx950's packed
+// conversion instruction (v_cvt_pk_bf16_f32).  It was checked on the device over all 2^32
+// float32 patterns against the integer formulation -- add 0x7FFF plus the lowest kept bit
+// to the 32-bit pattern (a carry into the kept half exactly when the dropped half is above
+// the midpoint, or at it with an odd kept half); a NaN becomes the quiet NaN with the same
+// sign and top payload bits -- with no difference, denormals and NaNs included.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two values in one instruction: lo in bits 0..15, hi in bits 16..31.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.0f); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 

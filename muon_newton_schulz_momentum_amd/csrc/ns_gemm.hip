@@ -739,15 +739,24 @@ void ns_vs_kernel(NsArgs p) {
 #pragma unroll
                     for (int w = 0; w < 4; ++w) v[w] = dev::ns_combine(p.alpha, __builtin_bit_cast(float, ew[w]), p.gamma, v[w]);
                 }
-                res[i][j][q].x = (uint32_t)dev::f32_to_bf16(v[0]) | ((uint32_t)dev::f32_to_bf16(v[1]) << 16);
-                res[i][j][q].y = (uint32_t)dev::f32_to_bf16(v[2]) | ((uint32_t)dev::f32_to_bf16(v[3]) << 16);
+                res[i][j][q].x = dev::f32x2_to_bf16x2(v[0], v[1]);
+                res[i][j][q].y = dev::f32x2_to_bf16x2(v[2], v[3]);
             }
         }
     }
+    if (MODE == NS_POLY || MODE == NS_AXPY) lds_wait_barrier();   // E reads done before T is written
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec)) = res[i][j][q];
+    lds_wait_barrier();
     if (PERSIST) b_next = persistent_tile(blockIdx.x, gridDim.x, it + 1, p.total_tiles);
     if (PF) {
-        // The next tile's K step 0 goes out now, after the combine (so that it does not add
-        // to the epilogue's register peak) and ahead of this tile's stores: the
+        // The next tile's K step 0 goes out now, after the result tile is in LDS (so that it
+        // does not add to the epilogue's register peak) and ahead of this tile's stores: the
         // vector-memory counter retires in issue order and counts stores too, so the next
         // prologue then waits only for these loads, not for the stores to drain.
         // the staging registers' old contents are dead on every path from here (otherwise
@@ -777,15 +786,6 @@ void ns_vs_kernel(NsArgs p) {
             }
         }
     }
-    if (MODE == NS_POLY || MODE == NS_AXPY) lds_wait_barrier();   // E reads done before T is written
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec)) = res[i][j][q];
-    lds_wait_barrier();
     // the tile: 256 rows x 32 granules, whole rows per 32 lanes
     uint16_t* orow = out + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
 #pragma unroll
