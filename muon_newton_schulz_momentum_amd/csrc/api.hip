@@ -208,6 +208,7 @@ muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int
         const float a_ = abc[3 * it], b_ = abc[3 * it + 1], c_ = abc[3 * it + 2];
         uint16_t* nxt = (cur == xp) ? xq : xp;
         NsArgs g{};
+        g.sched = at<uint32_t>(p, c.off_sched);
         // A = X X^T
         g.opa = cur; g.opb = cur; g.ep = cur; g.out = am;
         g.stride_a = xs; g.stride_b = xs; g.stride_o = as;

@@ -75,6 +75,9 @@ struct NsArgs {
     int32_t total_tiles;
     float alpha;           // POLY: b (times A); AXPY: a (times X)
     float gamma;           // POLY: c (times the product); AXPY: 1
+    // persistent launches: 8 per-XCD tile counters and a finished count, zero at launch
+    // (the launch's last workgroup sets them back to zero)
+    uint32_t* sched;
 };
 
 // Whole Newton–Schulz of small matrices (canonical m <= 64, padded n <= SMALL_NS_MAX_N,

@@ -64,16 +64,23 @@ __device__ __forceinline__ int xcd_remap(int b, int g) {
 }
 
 // Persistent launches (one workgroup per CU, NUM_XCD | gridDim.x): workgroup w runs on XCD
-// w % NUM_XCD, and the XCD's workgroups walk its contiguous share of the tile order (the
-// shares of xcd_remap) together, so that the tiles one XCD runs at the same time are
-// neighbours in that order, as in the one-tile-per-workgroup launch.  -1 when done.
-__device__ __forceinline__ int persistent_tile(int w, int g, int it, int total) {
-    const int xcd = w % NUM_XCD, local = w / NUM_XCD, per = g / NUM_XCD;
+// w % NUM_XCD (the hardware deals consecutive workgroup ids to the XCDs in turn).  The tile
+// order is cut into the contiguous XCD shares of xcd_remap, and each XCD's workgroups take
+// the tiles of its share one by one from a counter (so that the tiles one XCD runs at the
+// same time are neighbours in that order, as in the one-tile-per-workgroup launch, and a
+// slower CU simply takes fewer tiles); a workgroup whose share is used up takes tiles
+// from the other XCDs' shares.  Only atomic increments, no waiting: every workgroup stops
+// once all eight counters are past their shares.  -1 when done.
+__device__ __forceinline__ int grab_tile(uint32_t* sched, int xcd, int total) {
     const int q = total / NUM_XCD, r = total % NUM_XCD;
-    const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-    const int size = q + (xcd < r ? 1 : 0);
-    const int loc = local + per * it;
-    return loc < size ? start + loc : -1;
+    for (int k = 0; k < NUM_XCD; ++k) {
+        const int x = (xcd + k) % NUM_XCD;
+        const int start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+        const int size = q + (x < r ? 1 : 0);
+        const uint32_t loc = atomicAdd(&sched[x], 1u);
+        if ((int)loc < size) return start + (int)loc;
+    }
+    return -1;
 }
 
 // Tile order.  The 32 tiles an XCD runs at once should share as few operand panels as
@@ -505,11 +512,17 @@ void ns_vs_kernel(NsArgs p) {
   // persistent case the next tile's first K step is fetched into the staging registers
   // before the current tile's epilogue (see below)
   i32x4 sa[NCH], sb[NCH];
+  __shared__ int next_slot;                             // the next tile, from thread 0's grab
   int b_next = -1;
+  if (PERSIST) {
+      if (threadIdx.x == 0) next_slot = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
+      __syncthreads();
+      b_next = next_slot;
+  }
   for (int it = 0;; ++it) {
     int b;
     if (PERSIST) {
-        b = it == 0 ? persistent_tile(blockIdx.x, gridDim.x, 0, p.total_tiles) : b_next;
+        b = b_next;
         if (b < 0) break;
         if (it > 0) __syncthreads();                      // the last tile's LDS reads are done
     } else {
@@ -711,6 +724,11 @@ void ns_vs_kernel(NsArgs p) {
     auto tb = [](int r, int c) { return r * 512 + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2; };
     const int er = lane & 31, ec = 4 * (lane >> 5);
     lds_wait_barrier();                                   // every wave is done with the K stages
+    // the next tile: the atomic goes out now and its result is published to the workgroup
+    // at the barrier after the result tile is staged, so its latency hides behind the E
+    // load and the combine
+    int grabbed = -1;
+    if (PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
     if (MODE == NS_POLY || MODE == NS_AXPY) {
         const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
 #pragma unroll 4
@@ -752,8 +770,9 @@ void ns_vs_kernel(NsArgs p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec)) = res[i][j][q];
+    if (PERSIST && threadIdx.x == 0) next_slot = grabbed;
     lds_wait_barrier();
-    if (PERSIST) b_next = persistent_tile(blockIdx.x, gridDim.x, it + 1, p.total_tiles);
+    if (PERSIST) b_next = next_slot;
     if (PF) {
         // The next tile's K step 0 goes out now, after the result tile is in LDS (so that it
         // does not add to the epilogue's register peak) and ahead of this tile's stores: the
@@ -812,6 +831,16 @@ void ns_vs_kernel(NsArgs p) {
             *reinterpret_cast<bf16x8*>(omir + (int64_t)(c0 + x) * p.ldo + r0) = v8;
         }
     }
+  }
+  // The launch's last workgroup to finish sets the counters back to zero for the next
+  // launch (every other workgroup has taken its last, empty, grab before counting itself
+  // finished, so nothing reads them afterwards in this launch).
+  if (PERSIST && threadIdx.x == 0) {
+      __threadfence();
+      if (atomicAdd(&p.sched[NUM_XCD], 1u) == gridDim.x - 1) {
+#pragma unroll
+          for (int x = 0; x <= NUM_XCD; ++x) atomicExch(&p.sched[x], 0u);
+      }
   }
 }
 

@@ -76,6 +76,7 @@ void layout_region(Chunk& c, uint64_t base) {
     c.off_b = off;  off = align_up(off + ab, WS_ALIGN);
     c.off_part = off; off = align_up(off + (uint64_t)c.count * c.ew_tiles * 8ull, WS_ALIGN);
     c.off_inv = off;  off = align_up(off + (uint64_t)c.count * 8ull, WS_ALIGN);
+    c.off_sched = off; off = align_up(off + SCHED_BYTES, WS_ALIGN);
     c.region_off = base;
     c.region_bytes = off - base;
 }
@@ -258,7 +259,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     p->table_bytes = p->off_adam_segs + align_up((uint64_t)p->adam_segs.size() * sizeof(AdamSeg), WS_ALIGN);
     uint64_t total = p->table_bytes;
     for (const BucketGeo& g : geo)
-        total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 6 * WS_ALIGN;
+        total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 7 * WS_ALIGN;
     p->shared_regions = cap != 0 && total > cap;
     p->flags = flags;
     const bool pipeline = (flags & MUON_PLAN_PIPELINE) != 0;
@@ -281,7 +282,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
         if (p->shared_regions) {
             // one region of up to `room` bytes, or two of up to `room` each (double buffering)
             const uint64_t pm = per_matrix_bytes(g.mp, g.np, g.ew);
-            const uint64_t slack = (double_buffer ? 12 : 6) * WS_ALIGN;
+            const uint64_t slack = (double_buffer ? 14 : 7) * WS_ALIGN;
             uint64_t room = cap > p->table_bytes + slack ? cap - p->table_bytes - slack : 0;
             if (double_buffer) room /= 2;
             const int64_t fit = (int64_t)(room / pm);

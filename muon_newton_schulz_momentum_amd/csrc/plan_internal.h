@@ -42,6 +42,7 @@ struct Chunk {
     // workspace layout (byte offsets from the workspace base)
     uint64_t region_off, region_bytes;
     uint64_t off_xp, off_xq, off_a, off_b, off_part, off_inv;
+    uint64_t off_sched;      // tile-queue counters of the persistent product kernels (zero between launches)
     uint64_t off_table;      // this chunk's first table row
 };
 
@@ -128,6 +129,7 @@ void clear_error();
 constexpr int EW_TILE = 64;          // elementwise tile edge
 constexpr int SMALL_NS_MAX_N = 1024; // widest padded n of the fused small-matrix kernel
 constexpr uint64_t WS_ALIGN = 256;   // workspace sub-buffer alignment
+constexpr uint64_t SCHED_BYTES = 256; // per region: 8 per-XCD tile counters and a finished count (uint32)
 // MUON_PLAN_PIPELINE chunking: at most this many chunks per bucket, each with at least this
 // many SYRK workgroups
 constexpr int64_t PIPE_MAX_SPLIT = 8;

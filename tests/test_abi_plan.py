@@ -149,7 +149,7 @@ def test_workspace_size_formula():
         m, n, mp, np_, k = i["m"], i["n"], i["m_pad"], i["n_pad"], i["count"]
         ew = -(-m // 64) * -(-n // 64)
         al = lambda v: (v + 255) // 256 * 256  # noqa: E731
-        region = 2 * al(k * mp * np_ * 2) + 2 * al(k * mp * mp * 2) + al(k * ew * 8) + al(k * 8)
+        region = 2 * al(k * mp * np_ * 2) + 2 * al(k * mp * mp * 2) + al(k * ew * 8) + al(k * 8) + 256  # + tile counters
         assert i["region_bytes"] == region and i["region_offset"] == total
         total += region
     assert nb.value == total
