@@ -173,7 +173,7 @@ muon_status ns_prep(const muon_plan* p, const Chunk& c, int32_t steps, float eps
     double* inv = at<double>(p, c.off_inv);
     hipError_t e;
     {
-        FinalizeArgs f{at<const double>(p, c.off_part), inv, c.ew_tiles, (double)eps};
+        FinalizeArgs f{at<const double>(p, c.off_part), inv, c.ew_tiles, (double)eps, at<uint32_t>(p, c.off_sched)};
         TimedLaunch tl(p, MUON_KERNEL_NORM_FINALIZE, (double)c.count * c.ew_tiles * 8.0, s);
         e = launch_finalize(f, c.count, s);
         tl.done(s);

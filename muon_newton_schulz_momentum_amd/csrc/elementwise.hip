@@ -253,6 +253,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
 __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
     __shared__ double red[4];
     const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid < SCHED_WORDS) a.sched[tid] = 0u;
     const int64_t mat = blockIdx.x;
     const double* p = a.partials + mat * a.ew_tiles;
     double s = 0.0;

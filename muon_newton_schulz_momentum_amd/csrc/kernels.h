@@ -22,11 +22,17 @@ struct MomentumArgs {
     int32_t nesterov;      // 1: X0 = bf16(f32(beta*M_new + (1-beta)*G)) instead of bf16(M_new)
 };
 
+// Words of a chunk's tile-queue block (8 per-XCD counters and a finished count).
+constexpr int SCHED_WORDS = 9;
+
 struct FinalizeArgs {
     const double* partials;
     double* inv;           // per matrix: 1 / (sqrt(sum) + eps)
     int64_t ew_tiles;
     double eps;
+    // the chunk's tile-queue block, zeroed here before its product launches: in a region
+    // shared with other chunks, their data may have overwritten it since its last use
+    uint32_t* sched;
 };
 
 struct NormalizeArgs {
@@ -76,7 +82,8 @@ struct NsArgs {
     float alpha;           // POLY: b (times A); AXPY: a (times X)
     float gamma;           // POLY: c (times the product); AXPY: 1
     // persistent launches: 8 per-XCD tile counters and a finished count, zero at launch
-    // (the launch's last workgroup sets them back to zero)
+    // (the finalize kernel zeroes them before a chunk's first product launch, and each
+    // launch's last workgroup sets them back to zero for the next)
     uint32_t* sched;
 };
 
