@@ -299,3 +299,38 @@ def test_kernel_timing_records_launches(mm):
     assert n == K and ms > 0 and work == pytest.approx(K * 2 * 2.0 * 256 * 256 * 512)
     ms, n, work = plan.timing_read(L.MUON_KERNEL_MOMENTUM)
     assert n == 1 and work == 2 * 256 * 512 * 14
+
+
+def test_persistent_launches_in_a_shared_region_equal_unchunked(mm):
+    # Two buckets whose chunks each make persistent product launches (>= 512 tiles of
+    # 256 x 256) and share one workspace region under a cap: every chunk's tile counters
+    # sit inside the other bucket's buffers and must still start at zero (a stale counter
+    # skips tiles).  Bitwise equal to the unchunked plan, eagerly and in a graph replay.
+    harness, _ = mm
+    shapes = [(1024, 2048)] * 120 + [(2048, 2048)] * 16
+    base = _make(shapes, seed=15)
+    snap = _snapshot(base)
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+
+    def fresh():
+        return [ParamTensors(torch.from_numpy(s[0]).cuda(), torch.from_numpy(s[1]).cuda(),
+                             torch.from_numpy(s[2]).cuda()) for s in snap]
+    ps_full = fresh()
+    full = harness.Plan(ps_full)
+    ps_cap = fresh()
+    capped = harness.Plan(ps_cap, max_workspace_bytes=full.workspace_bytes // 2)
+    infos = [capped.chunk_info(c) for c in range(capped.n_chunks)]
+    assert capped.n_chunks >= 3 and all(i.shared_region == 1 for i in infos)
+    tri = {1024: 10, 2048: 36}                            # SYRK tiles per matrix
+    assert all(i.count * tri[i.m] >= 512 for i in infos), [(i.m, i.count) for i in infos]
+    g = capped.capture(0.95, 0.02, 0.1)
+    for step in range(2):
+        full.step(0.95, 0.02, 0.1)
+        if step == 0:
+            capped.step(0.95, 0.02, 0.1)
+        else:
+            g.launch()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ps_full, ps_cap)):
+            assert torch.equal(a.weight, b.weight) and torch.equal(a.momentum, b.momentum), (step, i)
+    g.close()
