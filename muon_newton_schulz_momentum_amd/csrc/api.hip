@@ -550,13 +550,14 @@ muon_step_config legacy_config(float beta, float a, float b, float c, int32_t st
     return k;
 }
 
-// The tile grid of a chunk must fit the kernels' int32 indexing, and one padded matrix
-// (X, A or B) the 32-bit byte offsets of the buffer loads.
+// The tile grid of a chunk must fit the kernels' int32 indexing, one padded matrix (X, A
+// or B) the 32-bit byte offsets of the buffer loads, and the chunk's rows the normaliser's
+// 32-bit row index.
 bool grid_fits(const Chunk& c) {
     const int64_t tm = c.mp / c.tile, tn = c.np / c.tile;
     const int64_t lim = int64_t(1) << 31;
     return c.count * tm * tn < lim && c.count * tm * (tm + 1) / 2 < lim && c.mp * c.np * 2 < lim &&
-           c.mp * c.mp * 2 < lim;
+           c.mp * c.mp * 2 < lim && c.count * c.mp < lim;
 }
 
 }  // namespace

@@ -281,37 +281,61 @@ __device__ __forceinline__ uint4 normalize_unit(uint4 in, int64_t c, int64_t n, 
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
+// The chunk's matrices are mp x np blocks one after another, so unit u (8 elements) is in
+// global row R = u / (np / 8) at element offset R * np + 8 * (u mod np / 8), and its matrix
+// is R / mp.  Per workgroup pass the base unit's row is found once (uniform, 64-bit); each
+// thread then divides only small 32-bit offsets.  (Two 64-bit divisions per unit made the
+// kernel bound by vector-ALU work rather than by HBM.)
+struct UnitPos {
+    int64_t off;      // element offset of the unit in the chunk's X buffers
+    int64_t mat;
+    bool live;        // inside the matrix's m x n region
+    uint32_t c;       // column of the unit's first element
+};
+
+__device__ __forceinline__ UnitPos unit_pos(const NormalizeArgs& a, int64_t r0, uint32_t k0, uint32_t d,
+                                            uint32_t upr) {
+    const uint32_t t = k0 + d;
+    const uint32_t q = t / upr;
+    const uint32_t k = t - q * upr;
+    const int64_t R = r0 + q;
+    const uint32_t mp = (uint32_t)a.mp;
+    const uint32_t Rm = (uint32_t)R;                  // a chunk has fewer than 2^31 rows (checked at bind)
+    const uint32_t mat = Rm / mp;
+    const uint32_t r = Rm - mat * mp;
+    UnitPos u;
+    u.c = k * 8u;
+    u.off = R * a.np + u.c;
+    u.mat = mat;
+    u.live = r < (uint32_t)a.m && u.c < (uint32_t)a.n;
+    return u;
+}
+
 // Each thread takes UPT units of 8 elements, one block-width apart, and issues all its
 // loads before the first store.
 constexpr int UPT = 4;
 
 __global__ __launch_bounds__(256) void normalize_kernel(NormalizeArgs a) {
-    const int64_t upr = a.np >> 3;             // 8-element units per row
-    const int64_t per_mat = a.mp * upr;
+    const uint32_t upr = (uint32_t)(a.np >> 3);          // 8-element units per row
     const int64_t span = (int64_t)gridDim.x * blockDim.x * UPT;
-    for (int64_t u0 = (int64_t)blockIdx.x * blockDim.x * UPT + threadIdx.x; u0 < a.total_units; u0 += span) {
+    for (int64_t ub = (int64_t)blockIdx.x * blockDim.x * UPT; ub < a.total_units; ub += span) {
+        const int64_t r0 = ub / upr;                      // uniform
+        const uint32_t k0 = (uint32_t)(ub - r0 * upr);
         uint4 in[UPT];
-        int64_t off[UPT], cc[UPT], mm[UPT];
-        bool live[UPT];
+        UnitPos pos[UPT];
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
-            const int64_t u = u0 + (int64_t)k * blockDim.x;
-            const int64_t mat = u / per_mat;
-            const int64_t rem = u - mat * per_mat;
-            const int64_t r = rem / upr;
-            const int64_t c = (rem - r * upr) * 8;
-            off[k] = mat * a.mp * a.np + r * a.np + c;
-            cc[k] = c;
-            mm[k] = mat;
-            live[k] = u < a.total_units && r < a.m && c < a.n;
-            in[k] = live[k] ? *reinterpret_cast<const uint4*>(a.src + off[k]) : make_uint4(0, 0, 0, 0);
+            const uint32_t d = threadIdx.x + (uint32_t)k * blockDim.x;
+            pos[k] = unit_pos(a, r0, k0, d, upr);
+            const bool ok = ub + d < a.total_units && pos[k].live;
+            in[k] = ok ? *reinterpret_cast<const uint4*>(a.src + pos[k].off) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < UPT; ++k) {
-            const int64_t u = u0 + (int64_t)k * blockDim.x;
-            if (u >= a.total_units) continue;
-            const uint4 out = live[k] ? normalize_unit(in[k], cc[k], a.n, a.inv[mm[k]]) : make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(a.dst + off[k]) = out;
+            const uint32_t d = threadIdx.x + (uint32_t)k * blockDim.x;
+            if (ub + d >= a.total_units) continue;
+            const uint4 out = pos[k].live ? normalize_unit(in[k], pos[k].c, a.n, a.inv[pos[k].mat]) : make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(a.dst + pos[k].off) = out;
         }
     }
 }
@@ -700,19 +724,17 @@ __global__ __launch_bounds__(256) void momentum_side_kernel(MomentumArgs a) {
 
 // One 8-element unit per thread and pass (normalize_kernel takes UPT at a time).
 __global__ __launch_bounds__(256) void normalize_side_kernel(NormalizeArgs a) {
-    const int64_t upr = a.np >> 3;
-    const int64_t per_mat = a.mp * upr;
+    const uint32_t upr = (uint32_t)(a.np >> 3);
     const int64_t span = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < a.total_units; u += span) {
-        const int64_t mat = u / per_mat;
-        const int64_t rem = u - mat * per_mat;
-        const int64_t r = rem / upr;
-        const int64_t c = (rem - r * upr) * 8;
-        const int64_t off = mat * a.mp * a.np + r * a.np + c;
+    for (int64_t ub = (int64_t)blockIdx.x * blockDim.x; ub < a.total_units; ub += span) {
+        const int64_t r0 = ub / upr;
+        const uint32_t k0 = (uint32_t)(ub - r0 * upr);
+        if (ub + threadIdx.x >= a.total_units) continue;
+        const UnitPos pos = unit_pos(a, r0, k0, threadIdx.x, upr);
         uint4 out = make_uint4(0, 0, 0, 0);
-        if (r < a.m && c < a.n)
-            out = normalize_unit(*reinterpret_cast<const uint4*>(a.src + off), c, a.n, a.inv[mat]);
-        *reinterpret_cast<uint4*>(a.dst + off) = out;
+        if (pos.live)
+            out = normalize_unit(*reinterpret_cast<const uint4*>(a.src + pos.off), pos.c, a.n, a.inv[pos.mat]);
+        *reinterpret_cast<uint4*>(a.dst + pos.off) = out;
     }
 }
 
