@@ -12,9 +12,9 @@
  *   5. the update is cast back to FP32 and applied to the weights.
  *
  * On one GPU the all-to-all exchanges of steps 2 and 4 have no counterpart: this library
- * takes one GPU's share of whole matrices.  The shape batching and the cached metadata
- * of that section ("parameter matrices of the same shape are packed into a batch";
- * "resharding index metadata is computed once and cached") become the plan below.
+ * takes one GPU's share of whole matrices.  Two points of that section become the plan
+ * below: matrices of one shape are processed together as a batch, and the indexing
+ * metadata of the resharding is worked out once and then reused every step.
  *
  * Memory and ownership
  *   The caller owns every device buffer: weights W, momenta M, gradients G and the

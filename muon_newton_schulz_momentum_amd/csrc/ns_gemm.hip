@@ -2,10 +2,10 @@
 //
 // One quintic Newton–Schulz step on a canonical m x n matrix X (m <= n) is
 //     A = X X^T,   B = b A + c A A,   X' = a X + B X.
-// The pages run this on whole momentum matrices with an operator built for the
-// symmetric intermediates ("Frontier Pre-training at Microsoft AI", method details
-// section 5, resharding step 3; "symmetry-aware Newton–Schulz kernels" in the recipe
-// page's section "How to Make Parameter Updates Faster and More Stable?").  Here:
+// The pages run this on whole momentum matrices with an operator that exploits the
+// symmetry of the intermediates ("Frontier Pre-training at Microsoft AI", method details
+// section 5, resharding step 3; the recipe page, section "How to Make Parameter Updates
+// Faster and More Stable?").  Here:
 //   * NS_SYRK  A = X X^T: only tiles (i, j) with i <= j are computed; each off-diagonal
 //              tile is stored twice (as itself and mirrored), so A is exactly symmetric.
 //   * NS_POLY  B = b A + c A A^T: A is symmetric, so A A = A A^T and the same

@@ -68,9 +68,10 @@ def bf16_round(x) -> np.ndarray:
     scaled back (exact).  Results of magnitude 2^128 or more overflow to infinity.
     NaN and infinities pass through.
 
-    READING: one rounding, directly from float64.  (The pages' word for the BF16 cast of
-    the momentum is literally "truncate-convert" in the notes page, section 5 step 1; the
-    other three pages only say "cast".  Round-to-nearest-even is taken for every cast.)
+    READING: one rounding, directly from float64.  (The notes page, section 5 step 1,
+    names the momentum's BF16 conversion with a term whose literal sense is truncation;
+    the other three pages speak of a plain cast.  Round-to-nearest-even is taken for
+    every cast.)
     """
     x = np.asarray(x, dtype=np.float64)
     out = x.copy()
