@@ -221,3 +221,24 @@ def test_pipeline_plan_splits_a_large_bucket_and_places_by_window():
     g.close()
     plan.close()
     ref.close()
+
+
+def test_pipeline_argument_checks_and_rebind():
+    import ctypes as C
+    from muon_newton_schulz_momentum_amd import binding as L, harness
+    ps = _params(SHAPES[:8], seed=750)
+    ref_ps = _clone(ps)
+    plan, ref = harness.Plan(ps), harness.Plan(ref_ps)
+    k, keep = harness.Plan.config(BETA, LR, WD)
+    k.pipeline = 2
+    assert L.muon_step_ex(plan._plan, -1, C.byref(k), None) == L.MUON_ERR_INVALID_ARG
+    assert b"pipeline" in L.muon_last_error()
+    # binding again (same workspace) keeps the plan's side stream and events usable
+    plan.bind()
+    plan.step_ex(BETA, LR, WD, pipeline=True)
+    ref.step_ex(BETA, LR, WD)
+    torch.cuda.synchronize()
+    _same(ps, ref_ps, plan, ref, "after rebind")
+    del keep
+    plan.close()
+    ref.close()
