@@ -60,6 +60,17 @@ def load_traffic(kernel: str, workload: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -218,6 +229,55 @@ def main(argv=None):
             "bound": "mfma" if mfma else "hbm",
         }
     plan.timing_enable(0)
+
+    # ---- per-bucket NS rates: each chunk's momentum, then its Newton-Schulz alone between
+    # two events (one stream; the chunks' times are summed per bucket) ------------------
+    per_bucket = {}
+    for ch in range(plan.n_chunks):
+        info = plan.chunk_info(ch)
+        plan.momentum_update(w.beta, chunk=ch, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plan.ns_batched(w.a, w.b, w.c, w.steps, w.eps, chunk=ch, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b = per_bucket.setdefault(info.bucket, {"m": info.m, "n": info.n, "matrices": 0, "chunks": 0, "ms": 0.0,
+                                                "alg": 0.0, "conv": 0.0, "fused_small": bool(info.fused_small)})
+        b["matrices"] += info.count
+        b["chunks"] += 1
+        b["ms"] += e0.elapsed_time(e1)
+        b["alg"] += info.flops_algorithmic * w.steps
+        b["conv"] += info.flops_conventional * w.steps
+    buckets_out = []
+    for b in sorted(per_bucket.values(), key=lambda v: -v["ms"]):
+        m, n = b["m"], b["n"]
+        ai = (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n) / (6 * m * n + 8 * m * m)   # FLOP/B per iteration
+        roof = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3)                              # TFLOP/s
+        alg_rate = b["alg"] / (b["ms"] * 1e-3) / 1e12
+        buckets_out.append({
+            "m": m, "n": n, "matrices": b["matrices"], "chunks": b["chunks"], "fused_small": b["fused_small"],
+            "ns_ms": round(b["ms"], 4),
+            "effective_tflops_conventional": round(b["conv"] / (b["ms"] * 1e-3) / 1e12, 2),
+            "algorithmic_tflops": round(alg_rate, 2),
+            "algorithmic_frac_of_peak": round(alg_rate / PEAK_BF16_TFLOPS, 4),
+            "roof_tflops": round(roof, 1), "bound": "mfma" if roof >= PEAK_BF16_TFLOPS else "hbm",
+            "frac_of_own_roof": round(alg_rate / roof, 4),
+        })
+
+    # ---- a plain device-to-device copy, for scale next to the elementwise kernels -------
+    cp_n = (1 << 30) // 4
+    cp_src = torch.ones(cp_n, dtype=torch.float32, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    cp_ms = []
+    for _ in range(6):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        cp_dst.copy_(cp_src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cp_ms.append(c0.elapsed_time(c1))
+    copy_gbs = 2 * (1 << 30) / (sorted(cp_ms[1:])[2] * 1e-3) / 1e9
+    del cp_src, cp_dst
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
     roofline = {
@@ -267,6 +327,7 @@ def main(argv=None):
         n_sample = sum(len(v) for v in sample.values())
         cpu = {
             "value": round(conv / oracle_step_s / 1e12, 6), "unit": "TFLOP/s", "cores": blas_threads(),
+            "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{n_sample} matrices (first, middle, last of each of {len(buckets)} buckets), "
                       f"one full float64 step each; step time extrapolated as sum over buckets of "
@@ -313,6 +374,8 @@ def main(argv=None):
         },
         "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
+        "buckets": buckets_out,
+        "device_copy_gbs": round(copy_gbs, 1),
         "parity": parity,
         "input_generation_s": round(gen_s, 2),
         "kernel_source_hash": kernel_source_hash(),
