@@ -255,12 +255,7 @@ muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32
     return st != MUON_OK ? st : ns_iterate(p, c, abc, steps, s);
 }
 
-// Algorithmic FLOPs of one Newton–Schulz iteration over a chunk (the three products,
-// the symmetric ones on one triangle).
-double ns_iter_flops(const Chunk& c) {
-    const double m = (double)c.m, n = (double)c.n;
-    return (double)c.count * (m * (m + 1.0) * n + m * m * (m + 1.0) + 2.0 * m * m * n);
-}
+double ns_iter_flops(const Chunk& c) { return muon::ns_iter_flops(c.count, c.m, c.n); }
 
 // The fused small-matrix kernel over the given chunks (all with Chunk::fused), in
 // launches of up to SMALL_NS_MAX_JOBS chunks: normaliser, normalisation and every
@@ -366,17 +361,12 @@ std::vector<int32_t> pipeline_chunks(const muon_plan* p) {
     return t;
 }
 
-// Estimates for placing work on the side stream: the products' algorithmic rate is taken
-// above what they reach and the side kernels' bandwidth below, so that a window is never
-// overestimated and side work does not outlast the products it hides behind.
-constexpr double EST_NS_FLOPS = 1.2e15;     // FLOP/s
-constexpr double EST_SIDE_BW = 1.5e12;      // B/s
+// Side-stream placement estimates (the constants and their bias are with the planner's).
 double est_ns_s(const Chunk& c, int32_t steps) { return steps * ns_iter_flops(c) / EST_NS_FLOPS; }
 double est_prep_s(const Chunk& c) {         // momentum + normalise bytes, side kernels
-    const double el = (double)c.count * c.m * c.n;
-    return el * ((c.grad_dtype == MUON_DTYPE_F32 ? 14.0 : 12.0) + 4.0) / EST_SIDE_BW;
+    return (double)c.count * c.m * c.n * prep_bytes_per_elem(c.grad_dtype) / EST_SIDE_BW;
 }
-double est_apply_s(const Chunk& c) { return (double)c.count * c.m * c.n * 10.0 / EST_SIDE_BW; }
+double est_apply_s(const Chunk& c) { return (double)c.count * c.m * c.n * APPLY_BYTES_PER_ELEM / EST_SIDE_BW; }
 
 // The whole step with two streams.  The pages overlap the exchange of the next batch of
 // matrices with the orthogonalisation of the current one ("Frontier Pre-training at
@@ -426,21 +416,15 @@ muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, co
         }
     }
 
-    // placement: window j (NS(u_j)) takes P_{j+1} and A_{j-1} if both fit, else whichever
-    // of the two fits (P first: an exposed P holds up the next window), else neither
-    std::vector<char> p_side(T, 0), a_side(T, 0);
+    // placement of P_{j+1} and A_{j-1} beside NS(u_j) (pipe_place)
+    std::vector<double> win(T), tp(T), ta(T);
     for (size_t j = 0; j < T; ++j) {
-        const double win = est_ns_s(ch(j), cfg.steps);
-        const double tp = j + 1 < T ? est_prep_s(ch(j + 1)) : 0.0;
-        const double ta = j > 0 ? est_apply_s(ch(j - 1)) : 0.0;
-        const bool has_p = j + 1 < T, has_a = j > 0;
-        if (has_p && has_a && tp + ta <= win) {
-            p_side[j + 1] = a_side[j - 1] = 1;
-        } else {
-            if (has_p && tp <= win) p_side[j + 1] = 1;
-            else if (has_a && ta <= win) a_side[j - 1] = 1;
-        }
+        win[j] = est_ns_s(ch(j), cfg.steps);
+        tp[j] = est_prep_s(ch(j));
+        ta[j] = est_apply_s(ch(j));
     }
+    std::vector<char> p_side, a_side;
+    pipe_place(win, tp, ta, p_side, a_side);
 
     const Chunk& c0 = ch(0);
     if ((st = momentum_chunk(p, c0, cfg, s)) != MUON_OK) return st;

@@ -32,8 +32,6 @@ void clear_error() { g_last_error.clear(); }
 
 namespace {
 
-// The update scale of a shape rule (MUON_SCALE_*), computed in float64 and rounded once
-// to float32.
 // Which optimizer a parameter takes (see muon_param_desc).
 constexpr int32_t ROLE_NONE = 0, ROLE_MUON = 1, ROLE_ADAMW = 2;
 int32_t param_role(const muon_param_desc& d) {
@@ -43,6 +41,8 @@ int32_t param_role(const muon_param_desc& d) {
     return d.exp_avg_sq ? ROLE_ADAMW : ROLE_NONE;
 }
 
+// The update scale of a shape rule (MUON_SCALE_*), computed in float64 and rounded once
+// to float32.
 float rule_scale(int32_t mode, int64_t rows, int64_t cols) {
     const double r = (double)rows, c = (double)cols;
     switch (mode) {
@@ -82,6 +82,52 @@ void layout_region(Chunk& c, uint64_t base) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// One shape bucket: canonical and padded shape, product tile, elementwise tiles per
+// matrix, gradient dtype and its parameters in plan order.
+struct BucketGeo { int64_t m, n, mp, np, ew; int32_t tile, gdt; std::vector<int64_t> members; };
+
+// The estimated time of a two-stream step over tiled chunks (bucket, count) in step order:
+// the first chunk's momentum and normaliser and the last one's apply at full speed, every
+// chunk's products, a fixed cost per chunk, the side-stream tasks that pipe_place leaves
+// on the main stream, and what the tasks it moves beside the products cost them.  Window sizes are estimated as at step time (algorithmic
+// FLOPs); a 256-tile chunk's products are timed by the waves of tiles each launch runs (x
+// tiles take ceil(x / EST_CUS) tile times), so that a split which adds a partial wave costs
+// what it costs.
+double est_pipelined_step(const std::vector<std::pair<const BucketGeo*, int64_t>>& seq) {
+    const size_t T = seq.size();
+    std::vector<double> win(T), prep(T), apply(T), prep_full(T), apply_full(T), ns(T);
+    const double cu_rate = EST_NS_FLOPS / (double)EST_CUS;
+    for (size_t j = 0; j < T; ++j) {
+        const BucketGeo& g = *seq[j].first;
+        const int64_t c = seq[j].second;
+        const double el = (double)c * (double)g.m * (double)g.n;
+        win[j] = EST_STEPS * ns_iter_flops(c, g.m, g.n) / EST_NS_FLOPS;
+        prep[j] = el * prep_bytes_per_elem(g.gdt) / EST_SIDE_BW;
+        apply[j] = el * APPLY_BYTES_PER_ELEM / EST_SIDE_BW;
+        prep_full[j] = el * prep_bytes_per_elem(g.gdt) / EST_FULL_BW;
+        apply_full[j] = el * APPLY_BYTES_PER_ELEM / EST_FULL_BW;
+        if (g.tile == TILE_256) {
+            const int64_t tm = g.mp / TILE_256, tn = g.np / TILE_256;
+            const double t_syrk = 2.0 * TILE_256 * TILE_256 * (double)g.np / cu_rate;
+            const double t_sq = 2.0 * TILE_256 * TILE_256 * (double)g.mp / cu_rate;   // POLY, AXPY
+            const double w_tri = (double)ceil_div(tm * (tm + 1) / 2 * c, EST_CUS);
+            const double w_full = (double)ceil_div(tm * tn * c, EST_CUS);
+            ns[j] = EST_STEPS * (w_tri * (t_syrk + t_sq) + w_full * t_sq);
+        } else {
+            ns[j] = win[j];
+        }
+    }
+    std::vector<char> p_side, a_side;
+    pipe_place(win, prep, apply, p_side, a_side);
+    double t = prep_full[0] + apply_full[T - 1];
+    for (size_t j = 0; j < T; ++j) {
+        t += ns[j] + EST_CHUNK_S;
+        if (j + 1 < T) t += (p_side[j + 1] ? EST_SIDE_COST : 1.0) * prep_full[j + 1];
+        if (j > 0) t += (a_side[j - 1] ? EST_SIDE_COST : 1.0) * apply_full[j - 1];
+    }
+    return t;
+}
 
 struct Interval {
     uintptr_t lo, hi;   // [lo, hi)
@@ -235,7 +281,6 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     p->n_buckets = (int32_t)buckets.size();
 
     // ---- per-bucket geometry and chunking ----------------------------------------------
-    struct BucketGeo { int64_t m, n, mp, np, ew; int32_t tile, gdt; std::vector<int64_t> members; };
     std::vector<BucketGeo> geo;
     for (auto& kv : buckets) {
         BucketGeo g;
@@ -252,23 +297,35 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
         g.members = kv.second;
         geo.push_back(std::move(g));
     }
+    const bool pipeline = (flags & MUON_PLAN_PIPELINE) != 0;
+    if (pipeline) {
+        // The two-stream step hides each chunk's neighbours' elementwise work behind the
+        // chunk's products, so the buckets with little product time per element (the
+        // smaller tiles) go last, after the edge chunk that ends the 256-tile buckets.
+        std::stable_partition(geo.begin(), geo.end(), [](const BucketGeo& g) { return g.tile == TILE_256; });
+    }
 
     // the start of the workspace: matrix table, AdamW entries, AdamW segments
     p->off_adam = align_up((uint64_t)p->n_included * sizeof(MatEntry), WS_ALIGN);
     p->off_adam_segs = p->off_adam + align_up((uint64_t)p->adam.size() * sizeof(AdamEntry), WS_ALIGN);
     p->table_bytes = p->off_adam_segs + align_up((uint64_t)p->adam_segs.size() * sizeof(AdamSeg), WS_ALIGN);
     uint64_t total = p->table_bytes;
+    // each chunk's region adds up to 7 sub-buffer alignments
+    const uint64_t chunks_per_bucket = pipeline ? (uint64_t)PIPE_MAX_CHUNKS : 1;
     for (const BucketGeo& g : geo)
-        total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 7 * WS_ALIGN;
+        total += per_matrix_bytes(g.mp, g.np, g.ew) * (uint64_t)g.members.size() + 7 * WS_ALIGN * chunks_per_bucket;
     p->shared_regions = cap != 0 && total > cap;
     p->flags = flags;
-    const bool pipeline = (flags & MUON_PLAN_PIPELINE) != 0;
     const bool double_buffer = p->shared_regions && pipeline;
 
-    int32_t bucket_id = 0;
-    for (const BucketGeo& g : geo) {
+    // chunk sizes per bucket, in plan order
+    std::vector<std::vector<int64_t>> sizes(geo.size());
+    std::vector<char> fused_b(geo.size(), 0);
+    for (size_t bi = 0; bi < geo.size(); ++bi) {
+        const BucketGeo& g = geo[bi];
         int64_t per_chunk = (int64_t)g.members.size();
         const bool fused = !(flags & MUON_PLAN_TILED_SMALL) && g.mp == 64 && g.np <= SMALL_NS_MAX_N;
+        fused_b[bi] = fused;
         if (pipeline && !fused) {
             // The two-stream step hides a chunk's neighbours' elementwise work behind its
             // products, which needs several chunks per large bucket: up to PIPE_MAX_SPLIT,
@@ -300,9 +357,69 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
         const int64_t total_m = (int64_t)g.members.size();
         const int64_t nchunks = ceil_div(total_m, per_chunk);
         // balanced split: chunk sizes differ by at most one
+        for (int64_t c = 0; c < nchunks; ++c) sizes[bi].push_back(total_m / nchunks + (c < total_m % nchunks ? 1 : 0));
+    }
+    if (pipeline) {
+        // Edge chunks.  In the two-stream step the first tiled chunk's momentum and
+        // normaliser run before any product and the last one's apply after all of them, at
+        // full speed and alone.  So a smaller chunk is split off the front of the first
+        // 256-tile chunk and off the back of the last one (the same chunk when there is one),
+        // each of the size that minimises the estimated step time (0: no split).
+        size_t bf = geo.size(), bl = geo.size();
+        for (size_t bi = 0; bi < geo.size(); ++bi)
+            if (!fused_b[bi] && geo[bi].tile == TILE_256) { if (bf == geo.size()) bf = bi; bl = bi; }
+        auto sequence = [&]() {
+            std::vector<std::pair<const BucketGeo*, int64_t>> seq;
+            for (size_t bi = 0; bi < geo.size(); ++bi)
+                if (!fused_b[bi])
+                    for (const int64_t c : sizes[bi]) seq.emplace_back(&geo[bi], c);
+            return seq;
+        };
+        if (bf < geo.size()) {
+            // sizes[bf] and sizes[bl] with head chunk h and tail chunk t (0: none); the same
+            // bucket vector when bf == bl
+            const std::vector<int64_t> first = sizes[bf], last = sizes[bl];
+            auto apply = [&](int64_t h, int64_t t) {
+                sizes[bf] = first;
+                if (bl != bf) sizes[bl] = last;
+                std::vector<int64_t>& f = sizes[bf];
+                if (h > 0) { f.front() -= h; f.insert(f.begin(), h); }
+                std::vector<int64_t>& l = sizes[bl];
+                if (t > 0) { l.back() -= t; l.push_back(t); }
+            };
+            // a head h and a tail t of the same single chunk must leave at least one matrix
+            const bool one = bf == bl && first.size() == 1;
+            const int64_t n_head = first.front();
+            auto n_tail = [&](int64_t hh) { return one ? first.back() - hh : last.back(); };
+            // coordinate descent: the best head for the current tail, then the best tail for
+            // that head, for a few rounds (no round raises the estimate)
+            int64_t h = 0, t = 0;
+            apply(0, 0);
+            double best = est_pipelined_step(sequence());
+            for (int round = 0; round < 3; ++round) {
+                const int64_t h0 = h, t0 = t;
+                for (int64_t e = 1; e < n_head - (one ? t : 0); ++e) {
+                    apply(e, t);
+                    const double v = est_pipelined_step(sequence());
+                    if (v < best) { best = v; h = e; }
+                }
+                for (int64_t e = 1; e < n_tail(h); ++e) {
+                    apply(h, e);
+                    const double v = est_pipelined_step(sequence());
+                    if (v < best) { best = v; t = e; }
+                }
+                if (h == h0 && t == t0) break;
+            }
+            apply(h, t);
+        }
+    }
+
+    int32_t bucket_id = 0;
+    for (size_t bi = 0; bi < geo.size(); ++bi) {
+        const BucketGeo& g = geo[bi];
+        const bool fused = fused_b[bi];
         int64_t start = 0;
-        for (int64_t c = 0; c < nchunks; ++c) {
-            const int64_t cnt = total_m / nchunks + (c < total_m % nchunks ? 1 : 0);
+        for (const int64_t cnt : sizes[bi]) {
             Chunk ch{};
             ch.bucket = bucket_id; ch.grad_dtype = g.gdt;
             ch.m = g.m; ch.n = g.n; ch.mp = g.mp; ch.np = g.np; ch.tile = g.tile;

@@ -134,6 +134,55 @@ constexpr uint64_t SCHED_BYTES = 256; // per region: 8 per-XCD tile counters and
 // many SYRK workgroups
 constexpr int64_t PIPE_MAX_SPLIT = 8;
 constexpr int64_t PIPE_MIN_WG = 2048;
+// chunks per bucket the planner may make: the pipeline split and two edge chunks
+constexpr int64_t PIPE_MAX_CHUNKS = PIPE_MAX_SPLIT + 2;
+
+// Estimates for the two-stream step (placement on the side stream at step time, edge
+// chunks at plan time).  The products' algorithmic rate is taken above what they reach and
+// the side kernels' bandwidth below, so that a window is never overestimated and side work
+// does not outlast the products it hides behind.
+constexpr double EST_NS_FLOPS = 1.2e15;     // FLOP/s, the product kernels
+constexpr double EST_SIDE_BW = 1.5e12;      // B/s, the side-stream elementwise kernels
+constexpr double EST_FULL_BW = 5.0e12;      // B/s, the full-speed elementwise kernels
+constexpr double EST_CHUNK_S = 1.0e-4;      // s, fixed cost of one more chunk (launches, ramps)
+constexpr double EST_SIDE_COST = 0.5;       // what side work costs the products beside it, as a
+                                            // fraction of its one-stream time (measured)
+constexpr int64_t EST_CUS = 256;            // compute units: one 256-tile workgroup each
+constexpr int32_t EST_STEPS = 5;            // Newton–Schulz iterations assumed at plan time
+
+// Algorithmic FLOPs of one Newton–Schulz iteration over `count` canonical m x n matrices
+// (the three products, the symmetric ones on one triangle).
+inline double ns_iter_flops(int64_t count, int64_t m_, int64_t n_) {
+    const double m = (double)m_, n = (double)n_;
+    return (double)count * (m * (m + 1.0) * n + m * m * (m + 1.0) + 2.0 * m * m * n);
+}
+// Bytes per element of the elementwise passes: momentum with the normaliser, and apply.
+inline double prep_bytes_per_elem(int32_t grad_dtype) { return (grad_dtype == MUON_DTYPE_F32 ? 14.0 : 12.0) + 4.0; }
+constexpr double APPLY_BYTES_PER_ELEM = 10.0;
+
+// Side-stream placement of the two-stream step, for tiled chunks 0 .. T-1 in step order.
+// window[j]: estimated time of chunk j's products; prep[j], apply[j]: estimated side-stream
+// time of chunk j's momentum with normaliser, and of its apply.  Window j takes P_{j+1} and
+// A_{j-1} if both fit, else whichever of the two fits (P first: a P left on the main stream
+// holds up the next window), else neither.  Sets p_side[j] / a_side[j] for the tasks that
+// go to the side stream.
+inline void pipe_place(const std::vector<double>& window, const std::vector<double>& prep,
+                       const std::vector<double>& apply, std::vector<char>& p_side, std::vector<char>& a_side) {
+    const size_t T = window.size();
+    p_side.assign(T, 0);
+    a_side.assign(T, 0);
+    for (size_t j = 0; j < T; ++j) {
+        const bool has_p = j + 1 < T, has_a = j > 0;
+        const double tp = has_p ? prep[j + 1] : 0.0, ta = has_a ? apply[j - 1] : 0.0;
+        if (has_p && has_a && tp + ta <= window[j]) {
+            p_side[j + 1] = a_side[j - 1] = 1;
+        } else if (has_p && tp <= window[j]) {
+            p_side[j + 1] = 1;
+        } else if (has_a && ta <= window[j]) {
+            a_side[j - 1] = 1;
+        }
+    }
+}
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -367,27 +367,87 @@ def test_adamw_parameters_are_planned_by_role():
     L.muon_plan_destroy(p)
 
 
+def _unsplit_edges(sizes, want):
+    """The balanced split of `want` chunks that `sizes` came from (merging a head chunk
+    into the next one and a tail chunk into the one before), or None."""
+    for head in (0, 1):
+        for tail in (0, 1):
+            v = list(sizes)
+            if head and len(v) > 1:
+                v = [v[0] + v[1]] + v[2:]
+            elif head:
+                continue
+            if tail and len(v) > 1:
+                v = v[:-2] + [v[-2] + v[-1]]
+            elif tail:
+                continue
+            if len(v) == want and max(v) - min(v) <= 1:
+                return v
+    return None
+
+
 def test_pipeline_plans_split_large_buckets():
     # up to 8 chunks per bucket, each with at least 2048 SYRK workgroups (upper-triangle
-    # tiles of 256 x 256: 10 for m = 1024, 36 for m = 2048, 595 for m = 8704)
+    # tiles of 256 x 256: 10 for m = 1024, 36 for m = 2048, 595 for m = 8704), then at most
+    # one edge chunk split off each end of the 256-tile buckets' run
     cases = [((1024, 4096), 1536, 7), ((2048, 2048), 96, 1), ((2048, 2048), 200, 3), ((8704, 8704), 4, 1),
              ((2048, 2048), 5000, 8), ((64, 512), 3000, 1)]
     for shape, count, want in cases:
-        for flags, expect in ((0, 1), (L.MUON_PLAN_PIPELINE, want)):
+        for flags in (0, L.MUON_PLAN_PIPELINE):
             st, p = _plan(_descs([shape] * count), flags=flags)
             assert st == 0, L.muon_last_error()
             infos = _infos(p)
-            assert len(infos) == expect, (shape, count, flags, len(infos))
             sizes = [i["count"] for i in infos]
-            assert sum(sizes) == count and max(sizes) - min(sizes) <= 1
+            assert sum(sizes) == count
+            if flags == 0:
+                assert sizes == [count]
+            else:
+                assert _unsplit_edges(sizes, want) is not None, (shape, count, sizes)
+                if min(shape) < 1024:
+                    assert len(sizes) == want      # no edge chunks outside the 256-tile buckets
             assert all(i["shared_region"] == 0 for i in infos)
             L.muon_plan_destroy(p)
+
+
+def test_pipeline_edge_chunks_of_the_layer_ladder():
+    # 96 x (2048, 2048) and 72 x (2048, 5632): a smaller chunk off the front of the first
+    # bucket and off the back of the last, sized so that no product launch gains a partial
+    # wave of tiles on the 256 compute units; without the flag, one chunk per bucket
+    w = wl.get("ladder24")
+    shapes = [p.shape for p in w.params]
+    st, p = _plan(_descs(shapes))
+    assert [(i["m"], i["n"], i["count"]) for i in _infos(p)] == [(2048, 2048, 96), (2048, 5632, 72)]
+    L.muon_plan_destroy(p)
+    st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_PIPELINE)
+    infos = _infos(p)
+    L.muon_plan_destroy(p)
+    assert len(infos) == 4
+    a, b, c, d = (i["count"] for i in infos)
+    assert [(i["m"], i["n"]) for i in infos] == [(2048, 2048)] * 2 + [(2048, 5632)] * 2
+    assert a + b == 96 and c + d == 72 and a < b and d < c
+    waves = lambda x: -(-x // 256)
+    for (n, total, parts) in ((2048, 96, (a, b)), (5632, 72, (c, d))):
+        tri, full = 8 * 9 // 2, 8 * (n // 256)
+        for per in (tri, full):
+            assert sum(waves(per * k) for k in parts) == waves(per * total)
+
+
+def test_pipeline_plans_put_smaller_tiles_last():
+    # the 512-row router bucket (128 tiles) after the 256-tile expert chunks
+    shapes = [(512, 4096)] + [(1024, 4096)] * 300
+    st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_PIPELINE)
+    infos = _infos(p)
+    L.muon_plan_destroy(p)
+    assert infos[-1]["m"] == 512 and all(i["m"] == 1024 for i in infos[:-1])
+    st, p = _plan(_descs(shapes))
+    assert [i["m"] for i in _infos(p)] == [512, 1024]
+    L.muon_plan_destroy(p)
 
 
 def test_double_buffered_regions_under_a_cap():
     # tiled chunks alternate between two regions, each within half the remaining cap; the
     # fused small chunks stay in the first; without a binding cap (and buckets too small to
-    # split) the flag changes nothing
+    # split) the flag adds at most the edge chunks, each in a region of its own
     shapes = [(1024, 4096)] * 40 + [(4096, 1024)] * 20 + [(64, 512)] * 5
     st, p = _plan(_descs(shapes))
     full = C.c_uint64()
@@ -395,7 +455,14 @@ def test_double_buffered_regions_under_a_cap():
     plain = _infos(p)
     L.muon_plan_destroy(p)
     st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_PIPELINE)
-    assert st == 0 and _infos(p) == plain
+    piped = _infos(p)
+    assert st == 0 and len(plain) <= len(piped) <= len(plain) + 2
+    for key in ("m", "n"):
+        assert sorted(set(i[key] for i in piped)) == sorted(set(i[key] for i in plain))
+    assert sum(i["count"] for i in piped) == sum(i["count"] for i in plain)
+    assert all(i["shared_region"] == 0 for i in piped)
+    ends = sorted((i["region_offset"], i["region_offset"] + i["region_bytes"]) for i in piped)
+    assert all(ends[j][1] <= ends[j + 1][0] for j in range(len(ends) - 1))
     L.muon_plan_destroy(p)
     cap = full.value // 5
     st, p = _plan(_descs(shapes), cap=cap, flags=L.MUON_PLAN_PIPELINE)

@@ -194,16 +194,18 @@ def test_pipeline_with_adamw_params():
 
 
 def test_pipeline_plan_splits_a_large_bucket_and_places_by_window():
-    # a large expert-like bucket (split into two chunks by MUON_PLAN_PIPELINE) and a
-    # one-matrix router chunk: the router's window is far too short to hide the experts'
-    # apply, which then runs at full speed on the caller's stream; bits as one stream
+    # a large expert-like bucket (split into two chunks by MUON_PLAN_PIPELINE, plus edge
+    # chunks) and a one-matrix router chunk, which goes last: its window is far too short
+    # to hide the experts' apply, which then runs at full speed on the caller's stream;
+    # bits as one stream
     from muon_newton_schulz_momentum_amd import binding as L, harness
     shapes = [((1024, 1536), "f32")] * 420 + [((512, 1536), "f32")]
     ps = _params(shapes, seed=740)
     ref_ps = _clone(ps)
     plan = harness.Plan(ps, flags=L.MUON_PLAN_PIPELINE)
     ref = harness.Plan(ref_ps)
-    assert plan.n_chunks == 3 and ref.n_chunks == 2
+    assert 3 <= plan.n_chunks <= 5 and ref.n_chunks == 2
+    assert plan.chunk_info(plan.n_chunks - 1).m == 512
     anchor = 0
     snap = _snap(ps[anchor])
     for step in range(2):
