@@ -130,11 +130,14 @@ typedef struct muon_plan_opts {
 /* Plan for the two-stream step (muon_step_config.pipeline), which hides one chunk's
  * neighbours' elementwise work behind its Newton–Schulz products and so needs several
  * chunks: a large bucket is split into up to 8 chunks, as many as keep at least 2048
- * SYRK workgroups per launch (the chunk sizes of one bucket differ by at most one).
- * With a workspace cap that splits buckets anyway, the chunks are laid out in two
- * regions of at most half the remaining cap each, alternating between consecutive tiled
- * chunks, so that one chunk can be prepared while the previous one is orthogonalised.
- * Results do not depend on the chunking. */
+ * SYRK workgroups per launch (sizes differing by at most one).  The buckets of 256-row
+ * output tiles (m >= 1024) come first, and a smaller chunk may be split off the front of
+ * the first such chunk and off the back of the last one (their elementwise work is the
+ * part nothing hides), sized by an estimate of the step time that the plan computes from
+ * the shapes alone.  With a workspace cap that splits buckets anyway, the chunks are laid
+ * out in two regions of at most half the remaining cap each, alternating between
+ * consecutive tiled chunks, so that one chunk can be prepared while the previous one is
+ * orthogonalised.  Results do not depend on the chunking. */
 #define MUON_PLAN_PIPELINE 2u
 
 typedef struct muon_plan muon_plan;
