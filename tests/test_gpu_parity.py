@@ -288,6 +288,47 @@ def test_ladder24_sampled_matrices(mm):
     print(f"ladder24 sampled: worst NS rel err {worst:.2e}")
 
 
+def test_ladder24_bench_configuration(mm):
+    """The benchmark's timed configuration at full size: the two-stream plan (with its
+    edge chunks) and step, eagerly and as a graph replay from the same state.  Sampled
+    matrices from every chunk, at the chunk boundaries, both orientations."""
+    harness, wl = mm
+    from muon_newton_schulz_momentum_amd import binding as L
+    w = wl.get("ladder24")
+    params = harness.make_params(w)
+    plan = harness.Plan(params, flags=L.MUON_PLAN_PIPELINE)
+    chunk_of = [plan.param_info(i).chunk for i in range(len(params))]
+    sample = set()
+    for ch in range(plan.n_chunks):
+        members = [i for i, c in enumerate(chunk_of) if c == ch]
+        sample |= {members[0], members[-1]}
+    sample = sorted(sample | {4, 6})
+    assert plan.n_chunks >= 2 and len(sample) >= 2 * plan.n_chunks
+    snap = {i: (_host(params[i].weight), _host(params[i].momentum), _host(params[i].grad)) for i in sample}
+    w0 = [p.weight.clone() for p in params]
+    m0 = [p.momentum.clone() for p in params]
+    kw = dict(a=A, b=B, c=C, steps=K, eps=EPS)
+    plan.step_ex(w.beta, w.lr, w.wd, pipeline=True, **kw)
+    torch.cuda.synchronize()
+    worst = _check_step(plan, params, snap, w.beta, w.lr, w.wd, indices=sample)
+    eager = {i: (params[i].weight.clone(), params[i].momentum.clone(), plan.output_oriented(i).clone())
+             for i in sample}
+    g = plan.capture_ex(w.beta, w.lr, w.wd, pipeline=True, **kw)
+    for p, a, b in zip(params, w0, m0):
+        p.weight.copy_(a)
+        p.momentum.copy_(b)
+    torch.cuda.synchronize()
+    g.launch()
+    torch.cuda.synchronize()
+    for i in sample:
+        W, M, O = eager[i]
+        assert torch.equal(params[i].weight, W) and torch.equal(params[i].momentum, M), i
+        assert torch.equal(plan.output_oriented(i), O), i
+    g.close()
+    plan.close()
+    print(f"ladder24 two-stream, {plan.n_chunks} chunks, {len(sample)} sampled: worst NS rel err {worst:.2e}")
+
+
 def test_kernel_timing_records_launches(mm):
     harness, _ = mm
     from muon_newton_schulz_momentum_amd import binding as L
