@@ -100,8 +100,8 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the path's sharding across GPUs is described, not built)"}))
+        print(json.dumps({"error": "the Muon step here runs on one GPU only; --gpus must be 1 "
+                                   "(no path across several GPUs is implemented)"}))
         return 2
     if args.steps < 1 or args.warmup < 1:
         print(json.dumps({"error": "--steps and --warmup must be >= 1"}))
