@@ -375,3 +375,37 @@ def test_persistent_launches_in_a_shared_region_equal_unchunked(mm):
         for i, (a, b) in enumerate(zip(ps_full, ps_cap)):
             assert torch.equal(a.weight, b.weight) and torch.equal(a.momentum, b.momentum), (step, i)
     g.close()
+
+
+def test_persistent_ragged_bucket_equals_one_tile_per_workgroup(mm):
+    # 40 matrices of 1100 x 2300 pad to 1280 x 2304: 5 x 9 tiles of 256, a tile grid that
+    # is not a multiple of the 8-row tile groups.  The bucket's products run persistent
+    # (600 SYRK and poly tiles, 1800 axpy tiles); two of its matrices alone run one tile
+    # per workgroup (30 and 90 tiles).  The outputs of those two are bitwise the same in
+    # both launches (a matrix's result does not depend on its batch), and two matrices of
+    # the large batch are checked against the oracle.
+    harness, _ = mm
+    shapes = [(1100, 2300)] * 20 + [(2300, 1100)] * 20
+    base = _make(shapes, seed=41)
+    snap = _snapshot(base)
+    from muon_newton_schulz_momentum_amd.harness import ParamTensors
+
+    def fresh(idx):
+        return [ParamTensors(torch.from_numpy(snap[i][0]).cuda(), torch.from_numpy(snap[i][1]).cuda(),
+                             torch.from_numpy(snap[i][2]).cuda()) for i in idx]
+    big_ps = fresh(range(len(shapes)))
+    big = harness.Plan(big_ps)
+    info = big.chunk_info(0)
+    assert big.n_chunks == 1 and info.tile == 256 and info.m_pad == 1280 and info.n_pad == 2304
+    assert info.count * 15 >= 512                      # persistent launches
+    pair = [0, 39]
+    small_ps = fresh(pair)
+    small = harness.Plan(small_ps)
+    assert small.chunk_info(0).count * 15 < 512        # one tile per workgroup
+    for plan in (big, small):
+        _run(plan, 0.95, 0.02, 0.1)
+    for j, i in enumerate(pair):
+        assert torch.equal(big.output_oriented(i), small.output_oriented(j)), i
+        assert torch.equal(big_ps[i].weight, small_ps[j].weight), i
+    worst = _check_step(big, big_ps, snap, 0.95, 0.02, 0.1, indices=[5, 30])
+    print(f"persistent ragged bucket: worst NS rel err {worst:.2e}")
