@@ -499,3 +499,62 @@ def test_unknown_plan_flags_are_refused():
     st, p = _plan(_descs([(128, 256)]), flags=1 << 7)
     assert st == L.MUON_ERR_INVALID_ARG and not p.value
     assert b"flag" in L.muon_last_error()
+
+
+def test_pipeline_plans_of_random_bucket_mixes_are_well_formed():
+    # Many seeded shape mixes, with and without a workspace cap: every matrix lands in
+    # exactly one chunk, no chunk is empty, chunks of one bucket are contiguous and
+    # together hold the bucket, the 256-tile buckets come before the others, tiled chunks
+    # under a cap alternate between two regions, and the workspace stays within the cap.
+    rng = np.random.default_rng(20261202)
+    dims = [64, 96, 200, 512, 1024, 1100, 2048, 3000, 4096]
+    for trial in range(40):
+        nb = int(rng.integers(1, 5))
+        shapes = []
+        for _ in range(nb):
+            r, c = (int(x) for x in rng.choice(dims, 2))
+            shapes += [(r, c)] * int(rng.integers(1, 120))
+        rng.shuffle(shapes)
+        st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_PIPELINE)
+        assert st == 0, (trial, L.muon_last_error())
+        full = C.c_uint64()
+        L.muon_plan_workspace_bytes(p, C.byref(full))
+        L.muon_plan_destroy(p)
+        for cap in (0, full.value // 3):
+            st, p = _plan(_descs(shapes), cap=cap, flags=L.MUON_PLAN_PIPELINE)
+            if st == L.MUON_ERR_WORKSPACE_TOO_SMALL:
+                continue
+            assert st == 0, (trial, cap, L.muon_last_error())
+            infos = _infos(p)
+            assert all(i["count"] >= 1 for i in infos)
+            assert sum(i["count"] for i in infos) == len(shapes)
+            seen, order = set(), []
+            for i in infos:
+                if not order or order[-1] != i["bucket"]:
+                    assert i["bucket"] not in seen, "chunks of one bucket are contiguous"
+                    order.append(i["bucket"])
+                    seen.add(i["bucket"])
+            want = {}
+            for r, c in shapes:
+                key = (min(r, c), max(r, c))
+                want[key] = want.get(key, 0) + 1
+            got = {}
+            for i in infos:
+                got[(i["m"], i["n"])] = got.get((i["m"], i["n"]), 0) + i["count"]
+            assert got == want
+            tiles = [i["tile"] for i in infos if not i["fused_small"]]
+            assert tiles == sorted(tiles, key=lambda t: t != 256), "256-tile buckets first"
+            for k in range(len(shapes)):
+                pi = _pinfo(p, k)
+                assert pi.included == 1 and 0 <= pi.slot < infos[pi.chunk]["count"]
+            nbytes = C.c_uint64()
+            L.muon_plan_workspace_bytes(p, C.byref(nbytes))
+            if cap:
+                assert nbytes.value <= cap
+                tiled = [i for i in infos if not i["fused_small"]]
+                if tiled and tiled[0]["shared_region"]:
+                    offs = [i["region_offset"] for i in tiled]
+                    assert all(offs[j] != offs[j - 1] for j in range(1, len(offs)))
+            for i in infos:
+                assert i["region_offset"] + i["region_bytes"] <= nbytes.value
+            L.muon_plan_destroy(p)
