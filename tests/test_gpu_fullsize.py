@@ -213,3 +213,56 @@ def test_moe_slice_full_size_graph():
             assert torch.equal(params[i].weight, W_graph[i]), f"graph and eager step differ: {w.params[i].name}"
     print(f"moe_slice: {len(sample)} sampled matrices, worst NS rel err {worst:.2e}")
     plan.close()
+
+
+@pytest.mark.timeout(900)
+def test_moe_slice_full_size_two_stream_graph():
+    """The benchmark's configuration of the 261 GB slice: a two-stream plan (edge chunks,
+    router and gate buckets last) under an 8 GiB cap, so tiled chunks alternate between
+    two workspace regions; the pipelined step captured as one graph and replayed once.
+    Sampled matrices are then re-stepped chunk by chunk on one stream, which must give the
+    graph's weights bitwise, and checked against the oracle."""
+    from muon_newton_schulz_momentum_amd import binding as L, harness
+
+    def pick(w):
+        names = [p.name for p in w.params]
+        lo, hi = _scale_extremes(w)
+        want = ["l0.q", "l2.shared.down", "l1.k", "l3.k", "l3.router", "l1.head_gate", "l2.shared_gate",
+                "l0.e0.up", "l3.e511.gate"]
+        return sorted({names.index(n) for n in want} | {lo, hi})
+    cap = 8 * GiB
+    w, params, sample, snap = _setup("moe_slice", pick, reserve=cap + 2 * GiB)
+    plan = harness.Plan(params, max_workspace_bytes=cap, flags=L.MUON_PLAN_PIPELINE)
+    infos = [plan.chunk_info(c) for c in range(plan.n_chunks)]
+    tiled = [c for c, i in enumerate(infos) if not i.fused_small]
+    assert all(infos[c].shared_region for c in tiled)
+    offs = [infos[c].region_offset for c in tiled]
+    assert len(set(offs)) == 2 and all(offs[j] != offs[j - 1] for j in range(1, len(offs)))
+    assert [infos[c].tile for c in tiled] == sorted((infos[c].tile for c in tiled), key=lambda t: t != 256)
+    print(f"[moe_slice two-stream] {plan.n_chunks} chunks in {plan.workspace_bytes / GiB:.2f} GiB", flush=True)
+    g = plan.capture_ex(w.beta, w.lr, w.wd, pipeline=True, a=w.a, b=w.b, c=w.c, steps=w.steps, eps=w.eps)
+    g.launch()
+    torch.cuda.synchronize()
+    g.close()
+    W_graph = {}
+    for i in sample:
+        _, M0, G0 = snap[i]
+        M_ref, _ = orc.momentum_update(M0, G0, w.beta)
+        assert np.array_equal(_host(params[i].momentum).view(np.uint32), M_ref.view(np.uint32))
+        W_graph[i] = params[i].weight.clone()
+    by_chunk = {}
+    for i in sample:
+        by_chunk.setdefault(plan.param_info(i).chunk, []).append(i)
+    worst = 0.0
+    for ch, idx in sorted(by_chunk.items()):
+        for i in idx:
+            W0, M0, _ = snap[i]
+            params[i].weight.copy_(torch.from_numpy(W0))
+            params[i].momentum.copy_(torch.from_numpy(M0))
+        plan.step(w.beta, w.lr, w.wd, w.a, w.b, w.c, w.steps, w.eps, chunk=ch)
+        torch.cuda.synchronize()
+        worst = max(worst, _check(plan, params, snap, w, idx))
+        for i in idx:
+            assert torch.equal(params[i].weight, W_graph[i]), f"graph and eager step differ: {w.params[i].name}"
+    print(f"moe_slice two-stream: {len(sample)} sampled matrices in {len(by_chunk)} chunks, worst NS rel err {worst:.2e}")
+    plan.close()
