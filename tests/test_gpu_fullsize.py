@@ -1,7 +1,8 @@
 """Parity at the full sizes of the larger workloads, through the C ABI.
 
-Every matrix of the workload is stepped on the GPU in the launch configuration the
-benchmark uses; a sample of matrices is then checked against the float64 oracle:
+Every matrix of the workload is stepped on the GPU, with the one-stream plan and (for the
+MoE slice also) in the benchmark's two-stream configuration for that workload; a sample
+of matrices is then checked against the float64 oracle:
 momentum bitwise, the Newton–Schulz output within 1e-2 relative Frobenius (the whole
 five-iteration chain), and the apply bitwise given the GPU's own output.  The sample
 covers every bucket, both orientations and the extreme per-expert gradient scales.
