@@ -25,30 +25,23 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.0f); }
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
-
-// float64 -> bfloat16 bits with one rounding (to nearest, ties to even), so that a value
-// computed in float64 is not rounded twice on its way to bf16.
-//  * In bf16's normal range (|x| >= 2^-126) the 52-bit fraction is rounded to 7 bits on
-//    the integer pattern (the carry may step the exponent up); the result has at most
-//    8 significant bits and converts to float32 exactly, or to infinity past 2^128.
-//  * Below 2^-126 the step is a fixed 2^-133: scale, round half-even, scale back.
-__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
-    uint64_t u = (uint64_t)__double_as_longlong(x);
-    const uint32_t bexp = (uint32_t)(u >> 52) & 0x7ffu;
-    if (bexp == 0x7ffu) {
-        const uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
-        return (u & 0x000fffffffffffffull) ? (uint16_t)(sign | 0x7fc0u) : (uint16_t)(sign | 0x7f80u);
+// The normalisation of one 16-byte unit of 8 bf16 values: X = bf16(X0 * s), each product
+// in float32 and rounded to bf16 by the packed conversion; elements from `valid` on (the
+// padding past the matrix's last column) are zero.  Every kernel that normalises (one
+// stream, side stream, fused small matrices) uses this, so their results agree bitwise.
+__device__ __forceinline__ uint4 normalize8(uint4 in, int64_t valid, float s) {
+    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t y = f32x2_to_bf16x2(__uint_as_float(w[j] << 16) * s, __uint_as_float(w[j] & 0xffff0000u) * s);
+        if (2 * j + 1 >= valid) y &= (2 * j < valid) ? 0x0000ffffu : 0u;
+        o[j] = y;
     }
-    if (bexp >= 1023u - 126u) {
-        u += 0x00000fffffffffffull + ((u >> 45) & 1ull);
-        u &= ~0x00001fffffffffffull;
-        const float f = (float)__longlong_as_double((long long)u);
-        return (uint16_t)(__float_as_uint(f) >> 16);
-    }
-    const double r = ldexp(rint(ldexp(x, 133)), -133);
-    return (uint16_t)(__float_as_uint((float)r) >> 16);
+    return make_uint4(o[0], o[1], o[2], o[3]);
 }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
 // The epilogue combine of the Newton–Schulz products, alpha * E + gamma * P, as one
 // pinned sequence: gamma * P rounded to float32, then one fused multiply-add.  Written out

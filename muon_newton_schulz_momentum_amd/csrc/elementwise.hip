@@ -21,7 +21,6 @@ namespace {
 
 using dev::bf16_to_f32;
 using dev::f32_to_bf16;
-using dev::f64_to_bf16;
 
 constexpr int T = EW_TILE;      // 64
 constexpr int LDT = T + 8;      // LDS row stride (bf16) of a transpose tile: 144 B
@@ -268,17 +267,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
 }
 
 __device__ __forceinline__ uint4 normalize_unit(uint4 in, int64_t c, int64_t n, double s) {
-    const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-    uint32_t o[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if (c + j < n) {
-            const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
-            const uint32_t y = f64_to_bf16((double)bf16_to_f32(h) * s);
-            o[j >> 1] |= (j & 1) ? (y << 16) : y;
-        }
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
+    return dev::normalize8(in, n - c, (float)s);
 }
 
 // The chunk's matrices are mp x np blocks one after another, so unit u (8 elements) is in

@@ -87,20 +87,8 @@ __global__ __launch_bounds__(256) void ns_small_kernel(SmallNsArgs a) {
     for (int u = tid; u < SM_ROWS * CPR; u += 256) {
         const int r = u / CPR, c = (u - r * CPR) * 8;
         uint4 o4 = make_uint4(0, 0, 0, 0);
-        if (r < m && c < n) {
-            const uint4 in = *reinterpret_cast<const uint4*>(x0 + (int64_t)r * np + c);
-            const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-            uint32_t o[4] = {0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                if (c + j < n) {
-                    const uint32_t h = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
-                    const uint32_t y = dev::f64_to_bf16((double)dev::bf16_to_f32(h) * inv);
-                    o[j >> 1] |= (j & 1) ? (y << 16) : y;
-                }
-            }
-            o4 = make_uint4(o[0], o[1], o[2], o[3]);
-        }
+        if (r < m && c < n)
+            o4 = dev::normalize8(*reinterpret_cast<const uint4*>(x0 + (int64_t)r * np + c), n - c, (float)inv);
         *reinterpret_cast<uint4*>(X + xb(r, c)) = o4;
     }
     __syncthreads();
