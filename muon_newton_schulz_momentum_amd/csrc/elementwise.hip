@@ -543,17 +543,41 @@ __device__ __forceinline__ void momentum4_serial(float4& mn, uint16_t xb[4], flo
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Every side-kernel access is marked non-temporal (the instructions' nt bit): the data is
+// touched once per step, and streaming it through the caches with normal priority evicts
+// the operand slices that the product workgroups beside it reuse.  Measured on gfx950:
+// the products lose about 0.4 ms less per ladder24 step (the step 1.0 % faster, the MoE
+// bucket 1.7 %).
+constexpr int SIDE_CPOL = 2;
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 nt_ld_u2(const void* p) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 nt_ld_u4(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 nt_ld_f4(const float* p) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_st_f4(float* p, float4 f) {
+    const f32x4v v = {f.x, f.y, f.z, f.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(p));
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t side_rsrc(const void* base, uint64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)bytes, 0x00020000);
 }
 __device__ __forceinline__ float4 ld_f4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SIDE_CPOL);
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
 }
 __device__ __forceinline__ void st_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 f) {
     u32x4 v;
     v.x = __float_as_uint(f.x); v.y = __float_as_uint(f.y); v.z = __float_as_uint(f.z); v.w = __float_as_uint(f.w);
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, SIDE_CPOL);
 }
 
 // Four gradient elements starting at element i, widened to float32.
@@ -563,15 +587,15 @@ __device__ __forceinline__ void side_grad4(__amdgpu_buffer_rsrc_t rg, uint32_t i
         const float4 v = ld_f4(rg, i * 4u);
         out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
     } else {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rg, i * 2u, 0, 0);
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rg, i * 2u, 0, SIDE_CPOL);
         out[0] = bf16_to_f32(v.x & 0xffffu); out[1] = bf16_to_f32(v.x >> 16);
         out[2] = bf16_to_f32(v.y & 0xffffu); out[3] = bf16_to_f32(v.y >> 16);
     }
 }
 template <int GDT>
 __device__ __forceinline__ float side_grad1(__amdgpu_buffer_rsrc_t rg, uint32_t i) {
-    if (GDT == MUON_DTYPE_F32) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, i * 4u, 0, 0));
-    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, i * 2u, 0, 0));
+    if (GDT == MUON_DTYPE_F32) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg, i * 4u, 0, SIDE_CPOL));
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rg, i * 2u, 0, SIDE_CPOL));
 }
 
 template <int GDT>
@@ -623,7 +647,7 @@ __global__ __launch_bounds__(256) void momentum_side_kernel(MomentumArgs a) {
                 u32x2 v;
                 v.x = (uint32_t)xb[0] | ((uint32_t)xb[1] << 16);
                 v.y = (uint32_t)xb[2] | ((uint32_t)xb[3] << 16);
-                __builtin_amdgcn_raw_buffer_store_b64(v, rx, xi * 2u, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(v, rx, xi * 2u, 0, SIDE_CPOL);
             }
         } else {
             // 2-D tile, as momentum_kernel's general loop
@@ -652,9 +676,9 @@ __global__ __launch_bounds__(256) void momentum_side_kernel(MomentumArgs a) {
                             if (j < nvalid) {
                                 const uint32_t q = (base + (uint32_t)j) * 4u;
                                 const float gj = side_grad1<GDT>(rgr, base + (uint32_t)j);
-                                const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, q, 0, 0));
+                                const float m0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, q, 0, SIDE_CPOL));
                                 const float mn = momentum_elem(m0, gj, beta, omb);
-                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mn), rm, q, 0, 0);
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mn), rm, q, 0, SIDE_CPOL);
                                 xb[j] = x0_bits(mn, gj, nest, beta, omb);
                             }
                         }
@@ -672,11 +696,11 @@ __global__ __launch_bounds__(256) void momentum_side_kernel(MomentumArgs a) {
                             u32x2 v;
                             v.x = (uint32_t)xb[0] | ((uint32_t)xb[1] << 16);
                             v.y = (uint32_t)xb[2] | ((uint32_t)xb[3] << 16);
-                            __builtin_amdgcn_raw_buffer_store_b64(v, rx, xo, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b64(v, rx, xo, 0, SIDE_CPOL);
                         } else {
 #pragma unroll
                             for (int j = 0; j < 4; ++j)
-                                if (j < nvalid) __builtin_amdgcn_raw_buffer_store_b16(xb[j], rx, xo + 2u * (uint32_t)j, 0, 0);
+                                if (j < nvalid) __builtin_amdgcn_raw_buffer_store_b16(xb[j], rx, xo + 2u * (uint32_t)j, 0, SIDE_CPOL);
                         }
                     }
                 } else {
@@ -694,11 +718,11 @@ __global__ __launch_bounds__(256) void momentum_side_kernel(MomentumArgs a) {
                     const uint32_t xo = (xr * np + xc) * 2u;
                     if (xc + 16 <= rows) {
                         const u32x4* srcv = reinterpret_cast<const u32x4*>(&tr[q][seg]);
-                        __builtin_amdgcn_raw_buffer_store_b128(srcv[0], rx, xo, 0, 0);
-                        __builtin_amdgcn_raw_buffer_store_b128(srcv[1], rx, xo + 16u, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(srcv[0], rx, xo, 0, SIDE_CPOL);
+                        __builtin_amdgcn_raw_buffer_store_b128(srcv[1], rx, xo + 16u, 0, SIDE_CPOL);
                     } else {
                         for (uint32_t k = 0; xc + k < rows; ++k)
-                            __builtin_amdgcn_raw_buffer_store_b16(tr[q][seg + k], rx, xo + 2u * k, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b16(tr[q][seg + k], rx, xo + 2u * k, 0, SIDE_CPOL);
                     }
                 }
             }
@@ -720,10 +744,13 @@ __global__ __launch_bounds__(256) void normalize_side_kernel(NormalizeArgs a) {
         const uint32_t k0 = (uint32_t)(ub - r0 * upr);
         if (ub + threadIdx.x >= a.total_units) continue;
         const UnitPos pos = unit_pos(a, r0, k0, threadIdx.x, upr);
-        uint4 out = make_uint4(0, 0, 0, 0);
-        if (pos.live)
-            out = normalize_unit(*reinterpret_cast<const uint4*>(a.src + pos.off), pos.c, a.n, a.inv[pos.mat]);
-        *reinterpret_cast<uint4*>(a.dst + pos.off) = out;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (pos.live) {
+            const u32x4 in = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.src + pos.off));
+            const uint4 o = normalize_unit(make_uint4(in.x, in.y, in.z, in.w), pos.c, a.n, a.inv[pos.mat]);
+            v = u32x4{o.x, o.y, o.z, o.w};
+        }
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.dst + pos.off));
     }
 }
 
@@ -765,12 +792,12 @@ __global__ __launch_bounds__(256) void apply_side_kernel(ApplyArgs a) {
                 const uint32_t idx = e0 + (uint32_t)k * 1024u;
                 if (idx >= nel) break;
                 const uint32_t xi = (np == cols) ? idx : (idx / cols) * np + idx % cols;
-                const uint2 ov = *reinterpret_cast<const uint2*>(O + xi);
-                float4 w = *reinterpret_cast<const float4*>(e.w + idx);
+                const uint2 ov = nt_ld_u2(O + xi);
+                float4 w = nt_ld_f4(e.w + idx);
                 const float o[4] = {bf16_to_f32(ov.x & 0xffffu), bf16_to_f32(ov.x >> 16),
                                     bf16_to_f32(ov.y & 0xffffu), bf16_to_f32(ov.y >> 16)};
                 apply4_serial(w, o, d, u);
-                *reinterpret_cast<float4*>(e.w + idx) = w;
+                nt_st_f4(e.w + idx, w);
             }
             continue;
         }
@@ -785,8 +812,8 @@ __global__ __launch_bounds__(256) void apply_side_kernel(ApplyArgs a) {
                 const uint16_t* src = O + orow * a.np + ocol;
                 if (ocol + 16 <= e.rows) {
                     uint4* d4 = reinterpret_cast<uint4*>(&tr[q][seg]);
-                    d4[0] = reinterpret_cast<const uint4*>(src)[0];
-                    d4[1] = reinterpret_cast<const uint4*>(src)[1];
+                    d4[0] = nt_ld_u4(src);
+                    d4[1] = nt_ld_u4(src + 8);
                 } else {
                     for (int k = 0; ocol + k < e.rows; ++k) tr[q][seg + k] = src[k];
                 }
@@ -803,16 +830,16 @@ __global__ __launch_bounds__(256) void apply_side_kernel(ApplyArgs a) {
             if (e.trans) {
                 for (int j = 0; j < nvalid; ++j) o[j] = bf16_to_f32(tr[cg * 4 + j][rg + 16 * i]);
             } else if (nvalid == 4 && (a.np & 3) == 0) {
-                const uint2 v = *reinterpret_cast<const uint2*>(O + r * a.np + c);
+                const uint2 v = nt_ld_u2(O + r * a.np + c);
                 o[0] = bf16_to_f32(v.x & 0xffffu); o[1] = bf16_to_f32(v.x >> 16);
                 o[2] = bf16_to_f32(v.y & 0xffffu); o[3] = bf16_to_f32(v.y >> 16);
             } else {
                 for (int j = 0; j < nvalid; ++j) o[j] = bf16_to_f32(O[r * a.np + c + j]);
             }
             if (vec && nvalid == 4) {
-                float4 w = *reinterpret_cast<const float4*>(e.w + base);
+                float4 w = nt_ld_f4(e.w + base);
                 apply4_serial(w, o, d, u);
-                *reinterpret_cast<float4*>(e.w + base) = w;
+                nt_st_f4(e.w + base, w);
             } else {
                 for (int j = 0; j < nvalid; ++j) e.w[base + j] = apply_elem(e.w[base + j], o[j], d, u);
             }
