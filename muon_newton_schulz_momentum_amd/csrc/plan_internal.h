@@ -138,11 +138,13 @@ constexpr int64_t PIPE_MIN_WG = 2048;
 constexpr int64_t PIPE_MAX_CHUNKS = PIPE_MAX_SPLIT + 2;
 
 // Estimates for the two-stream step (placement on the side stream at step time, edge
-// chunks at plan time).  The products' algorithmic rate is taken above what they reach and
-// the side kernels' bandwidth below, so that a window is never overestimated and side work
-// does not outlast the products it hides behind.
-constexpr double EST_NS_FLOPS = 1.2e15;     // FLOP/s, the product kernels
-constexpr double EST_SIDE_BW = 1.5e12;      // B/s, the side-stream elementwise kernels
+// chunks at plan time), near the rates measured on gfx950 with the side kernels running:
+// the products' algorithmic rate 0.96-1.05 PFLOP/s, the side kernels 1.34-1.92 TB/s
+// (normaliser, apply, momentum).  More conservative values (1.2 PFLOP/s, 1.5 TB/s) left
+// applies that would have fitted on the caller's stream: the 261 GB MoE slice ran 2.4 %
+// slower with them.
+constexpr double EST_NS_FLOPS = 1.0e15;     // FLOP/s, the product kernels
+constexpr double EST_SIDE_BW = 1.6e12;      // B/s, the side-stream elementwise kernels
 constexpr double EST_FULL_BW = 5.0e12;      // B/s, the full-speed elementwise kernels
 constexpr double EST_CHUNK_S = 1.0e-4;      // s, fixed cost of one more chunk (launches, ramps)
 constexpr double EST_SIDE_COST = 0.5;       // what side work costs the products beside it, as a
