@@ -90,10 +90,10 @@ struct BucketGeo { int64_t m, n, mp, np, ew; int32_t tile, gdt; std::vector<int6
 // The estimated time of a two-stream step over tiled chunks (bucket, count) in step order:
 // the first chunk's momentum and normaliser and the last one's apply at full speed, every
 // chunk's products, a fixed cost per chunk, the side-stream tasks that pipe_place leaves
-// on the main stream, and what the tasks it moves beside the products cost them.  Window sizes are estimated as at step time (algorithmic
-// FLOPs); a 256-tile chunk's products are timed by the waves of tiles each launch runs (x
-// tiles take ceil(x / EST_CUS) tile times), so that a split which adds a partial wave costs
-// what it costs.
+// on the main stream, and what the tasks it moves beside the products cost them.  Window
+// sizes are estimated as at step time (algorithmic FLOPs); a 256-tile chunk's products are
+// timed by the waves of tiles each launch runs (x tiles take ceil(x / EST_CUS) tile
+// times), so that a split which adds a partial wave costs what it costs.
 double est_pipelined_step(const std::vector<std::pair<const BucketGeo*, int64_t>>& seq) {
     const size_t T = seq.size();
     std::vector<double> win(T), prep(T), apply(T), prep_full(T), apply_full(T), ns(T);
