@@ -344,13 +344,13 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
             if (double_buffer) room /= 2;
             const int64_t fit = (int64_t)(room / pm);
             if (fit < 1) {
+                const std::string msg = "one " + std::to_string(g.m) + "x" + std::to_string(g.n) +
+                                        " matrix needs " +
+                                        std::to_string((double_buffer ? 2 : 1) * pm + p->table_bytes + slack) +
+                                        " bytes of workspace" + (double_buffer ? " with double buffering" : "") +
+                                        "; the cap is " + std::to_string(cap);
                 delete p;
-                return set_error(MUON_ERR_WORKSPACE_TOO_SMALL,
-                                 "one " + std::to_string(g.m) + "x" + std::to_string(g.n) +
-                                     " matrix needs " +
-                                     std::to_string((double_buffer ? 2 : 1) * pm + p->table_bytes + slack) +
-                                     " bytes of workspace" + (double_buffer ? " with double buffering" : "") +
-                                     "; the cap is " + std::to_string(cap));
+                return set_error(MUON_ERR_WORKSPACE_TOO_SMALL, msg);
             }
             per_chunk = std::min(per_chunk, fit);
         }
