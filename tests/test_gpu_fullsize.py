@@ -267,3 +267,41 @@ def test_moe_slice_full_size_two_stream_graph():
             assert torch.equal(params[i].weight, W_graph[i]), f"graph and eager step differ: {w.params[i].name}"
     print(f"moe_slice two-stream: {len(sample)} sampled matrices in {len(by_chunk)} chunks, worst NS rel err {worst:.2e}")
     plan.close()
+
+
+@pytest.mark.timeout(900)
+def test_moe_bucket_full_size_two_stream():
+    """The MoE bucket in its benchmark configuration: a two-stream plan (experts split into
+    chunks with edge chunks, the router last), one pipelined eager step and one graph
+    replay from the same state, bitwise equal; sampled matrices from the first, a middle
+    and the last expert chunk and the router against the oracle."""
+    from muon_newton_schulz_momentum_amd import binding as L, harness
+
+    def pick(w):
+        lo, hi = _scale_extremes(w)
+        return sorted({0, 1, 2, lo, hi, len(w.params) // 2, len(w.params) - 2, len(w.params) - 1})
+    w, params, sample, snap = _setup("moe_bucket", pick, reserve=45 * GiB)
+    plan = harness.Plan(params, flags=L.MUON_PLAN_PIPELINE)
+    infos = [plan.chunk_info(c) for c in range(plan.n_chunks)]
+    assert plan.n_chunks >= 8 and infos[-1].m == 512 and all(i.m == 1024 for i in infos[:-1])
+    print(f"[moe_bucket two-stream] {plan.n_chunks} chunks: {[i.count for i in infos]}", flush=True)
+    w0 = [p.weight.clone() for p in params]
+    m0 = [p.momentum.clone() for p in params]
+    kw = dict(a=w.a, b=w.b, c=w.c, steps=w.steps, eps=w.eps)
+    plan.step_ex(w.beta, w.lr, w.wd, pipeline=True, **kw)
+    torch.cuda.synchronize()
+    worst = _check(plan, params, snap, w, sample)
+    eager = {i: (params[i].weight.clone(), params[i].momentum.clone()) for i in sample}
+    g = plan.capture_ex(w.beta, w.lr, w.wd, pipeline=True, **kw)
+    for p, a, b in zip(params, w0, m0):
+        p.weight.copy_(a)
+        p.momentum.copy_(b)
+    del w0, m0
+    torch.cuda.synchronize()
+    g.launch()
+    torch.cuda.synchronize()
+    g.close()
+    for i in sample:
+        assert torch.equal(params[i].weight, eager[i][0]) and torch.equal(params[i].momentum, eager[i][1]), i
+    print(f"moe_bucket two-stream: {len(sample)} sampled matrices, worst NS rel err {worst:.2e}")
+    plan.close()
