@@ -362,7 +362,7 @@ std::vector<int32_t> pipeline_chunks(const muon_plan* p) {
 }
 
 // Side-stream placement estimates (the constants and their bias are with the planner's).
-double est_ns_s(const Chunk& c, int32_t steps) { return steps * ns_iter_flops(c) / EST_NS_FLOPS; }
+double est_ns_s(const Chunk& c, int32_t steps) { return steps * ns_iter_flops(c) / est_ns_rate(c.m); }
 double est_prep_s(const Chunk& c) {         // momentum + normalise bytes, side kernels
     return (double)c.count * c.m * c.n * prep_bytes_per_elem(c.grad_dtype) / EST_SIDE_BW;
 }

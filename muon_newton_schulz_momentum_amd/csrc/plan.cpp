@@ -97,12 +97,12 @@ struct BucketGeo { int64_t m, n, mp, np, ew; int32_t tile, gdt; std::vector<int6
 double est_pipelined_step(const std::vector<std::pair<const BucketGeo*, int64_t>>& seq) {
     const size_t T = seq.size();
     std::vector<double> win(T), prep(T), apply(T), prep_full(T), apply_full(T), ns(T);
-    const double cu_rate = EST_NS_FLOPS / (double)EST_CUS;
     for (size_t j = 0; j < T; ++j) {
         const BucketGeo& g = *seq[j].first;
+        const double cu_rate = est_ns_rate(g.m) / (double)EST_CUS;
         const int64_t c = seq[j].second;
         const double el = (double)c * (double)g.m * (double)g.n;
-        win[j] = EST_STEPS * ns_iter_flops(c, g.m, g.n) / EST_NS_FLOPS;
+        win[j] = EST_STEPS * ns_iter_flops(c, g.m, g.n) / est_ns_rate(g.m);
         prep[j] = el * prep_bytes_per_elem(g.gdt) / EST_SIDE_BW;
         apply[j] = el * APPLY_BYTES_PER_ELEM / EST_SIDE_BW;
         prep_full[j] = el * prep_bytes_per_elem(g.gdt) / EST_FULL_BW;

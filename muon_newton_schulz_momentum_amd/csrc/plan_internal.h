@@ -139,11 +139,14 @@ constexpr int64_t PIPE_MAX_CHUNKS = PIPE_MAX_SPLIT + 2;
 
 // Estimates for the two-stream step (placement on the side stream at step time, edge
 // chunks at plan time), near the rates measured on gfx950 with the side kernels running:
-// the products' algorithmic rate 0.96-1.05 PFLOP/s, the side kernels 1.34-1.92 TB/s
-// (normaliser, apply, momentum).  More conservative values (1.2 PFLOP/s, 1.5 TB/s) left
-// applies that would have fitted on the caller's stream: the 261 GB MoE slice ran 2.4 %
-// slower with them.
-constexpr double EST_NS_FLOPS = 1.0e15;     // FLOP/s, the product kernels
+// the products' algorithmic rate by the short side m (about 0.9 PFLOP/s at m = 1024, 1.0
+// at 2048, 1.1 from 4096 on), the side kernels 1.34-1.92 TB/s (normaliser, apply,
+// momentum).  A single conservative 1.2 PFLOP/s and 1.5 TB/s left applies that would have
+// fitted on the caller's stream: the 261 GB MoE slice ran 2.4 % slower with them, and one
+// 1.0 PFLOP/s for every shape cost the MoE bucket (m = 1024) 1.8 %.
+inline double est_ns_rate(int64_t m) {      // FLOP/s, the product kernels
+    return m >= 4096 ? 1.1e15 : m >= 2048 ? 1.0e15 : m >= 1024 ? 0.9e15 : 0.5e15;
+}
 constexpr double EST_SIDE_BW = 1.6e12;      // B/s, the side-stream elementwise kernels
 constexpr double EST_FULL_BW = 5.0e12;      // B/s, the full-speed elementwise kernels
 constexpr double EST_CHUNK_S = 1.0e-4;      // s, fixed cost of one more chunk (launches, ramps)
