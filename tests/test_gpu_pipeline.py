@@ -244,3 +244,40 @@ def test_pipeline_argument_checks_and_rebind():
     del keep
     plan.close()
     ref.close()
+
+
+def test_random_shape_mixes_two_stream_equal_one_stream():
+    # Ten seeded random mixes of shapes (1 to 2300 rows and columns, both orientations, up
+    # to four buckets, fp32 or bf16 gradients): the two-stream step, uncapped and under a
+    # cap of a third of the one-stream workspace, bitwise equal to the one-stream step; the
+    # first and last matrix of each mix against the oracle.
+    from muon_newton_schulz_momentum_amd import binding as L, harness
+    rng = np.random.default_rng(7)
+    dims = [1, 5, 32, 64, 65, 96, 130, 200, 256, 300, 512, 700, 1024, 1100, 1536, 2048, 2300]
+    for trial in range(10):
+        shapes = []
+        for _ in range(int(rng.integers(1, 5))):
+            r, c = int(rng.choice(dims)), int(rng.choice(dims))
+            shapes += [(r, c)] * int(rng.integers(1, 40 if max(r, c) >= 1024 else 80))
+        gdt = "bf16" if rng.random() < 0.3 else "f32"
+        base = _params([(s, gdt) for s in shapes], seed=1000 + trial)
+        ref_ps = _clone(base)
+        ref = harness.Plan(ref_ps)
+        ref.step_ex(BETA, LR, WD)
+        torch.cuda.synchronize()
+        for cap in (0, ref.workspace_bytes // 3):
+            ps = _clone(base)
+            try:
+                plan = harness.Plan(ps, max_workspace_bytes=cap, flags=L.MUON_PLAN_PIPELINE)
+            except L.MuonError as e:
+                assert cap and e.status == L.MUON_ERR_WORKSPACE_TOO_SMALL, e
+                continue
+            plan.step_ex(BETA, LR, WD, pipeline=True)
+            torch.cuda.synchronize()
+            for i, (a, b) in enumerate(zip(ps, ref_ps)):
+                assert torch.equal(a.weight, b.weight) and torch.equal(a.momentum, b.momentum), (trial, cap, i)
+            plan.close()
+        snap = {i: _snap(base[i]) for i in (0, len(shapes) - 1)}
+        for i in snap:
+            _oracle_anchor(snap[i], ref, ref_ps, i)
+        ref.close()
