@@ -139,13 +139,13 @@ __device__ __forceinline__ void wait_vm() {
 // intrinsic, every later LDS read would first wait for all outstanding direct-to-LDS
 // loads (the compiler cannot tell that they target other stages), exposing the
 // global-load latency at every read.  Completion is therefore waited for explicitly
-// (wait_vm) before the barrier that publishes a stage.  The LDS base goes through M0;
-// nothing else in these kernels uses M0.
+// (wait_vm) before the barrier that publishes a stage.  The LDS base goes through M0,
+// which the statement declares clobbered, so the compiler keeps nothing of its own there.
 __device__ __forceinline__ void load_to_lds(const uint16_t* src, const uint16_t* lds_base) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)lds_base);
     // one wait state between writing M0 and the LDS-DMA instruction that reads it
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(base) : "memory", "m0");
 }
 
 // ds_read_b64_tr_b16: 4 x 4 blocks of 16-bit values transposed across each group of 16
