@@ -139,6 +139,12 @@ typedef struct muon_plan_opts {
  * consecutive tiled chunks, so that one chunk can be prepared while the previous one is
  * orthogonalised.  Results do not depend on the chunking. */
 #define MUON_PLAN_PIPELINE 2u
+/* Normalise in a separate pass instead of in the first iteration's operand loads.  By
+ * default a chunk of 256-row output tiles (m >= 1024) run for an odd number of iterations
+ * never writes the normalised X: its first SYRK and GEMM+axpy read X0 and normalise each
+ * value on its way into LDS, with the same arithmetic as the pass (bitwise the same
+ * result; this exists to show it). */
+#define MUON_PLAN_UNFUSED_NORMALIZE 4u
 
 typedef struct muon_plan muon_plan;
 
@@ -228,8 +234,16 @@ MUON_API muon_status muon_momentum_update(const muon_plan* plan, int32_t chunk, 
  * with bf16 MFMA products accumulated in float32.  A and B are symmetric; only their
  * upper-triangle tiles are computed and then mirrored.  The result O is left in the
  * workspace (see muon_plan_param_info).  The pages give no coefficients or step count;
- * (3.4445, -4.7750, 2.0315), 5 steps and eps = 1e-7 are the usual choice.
- * Errors: INVALID_ARG (chunk, steps < 1, non-finite scalars), NOT_BOUND, HIP. */
+ * (3.4445, -4.7750, 2.0315), 5 steps and eps = 1e-7 are the usual choice.  ("Frontier
+ * Pre-training at Microsoft AI", method details section 5, resharding step 3: the
+ * orthogonalisation of whole same-shape matrices with an operator for symmetric
+ * intermediates.)  For chunks of 256-row tiles (m >= 1024) and an odd step count the
+ * normalisation happens inside the first iteration's loads (bitwise the same X).
+ * The call consumes X0: the iterations overwrite it, so each call needs a muon_momentum_update
+ * of the chunk after the last Newton–Schulz call or step that touched it (or that touched
+ * another chunk in the same workspace region); the plan tracks this in the order calls are
+ * made and refuses the call otherwise.
+ * Errors: INVALID_ARG (chunk, steps < 1, non-finite scalars, no fresh X0), NOT_BOUND, HIP. */
 MUON_API muon_status muon_ns_batched(const muon_plan* plan, int32_t chunk, float a, float b, float c,
                             int32_t steps, float eps, void* stream);
 
@@ -252,7 +266,7 @@ MUON_API muon_status muon_step(const muon_plan* plan, int32_t chunk, float beta,
  * X = a_t X + B X.  The pages fix neither the coefficients nor their schedule;
  * muon_ns_batched is this call with the same (a, b, c) every iteration.
  * Errors: INVALID_ARG (chunk, coeffs NULL, steps outside [1, 1024], non-finite values,
- * eps < 0), NOT_BOUND, HIP. */
+ * eps < 0, no fresh X0 as for muon_ns_batched), NOT_BOUND, HIP. */
 MUON_API muon_status muon_ns_batched_schedule(const muon_plan* plan, int32_t chunk, const float* coeffs,
                                      int32_t steps, float eps, void* stream);
 

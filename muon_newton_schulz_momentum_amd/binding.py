@@ -56,6 +56,7 @@ MUON_OPT_NONE = 2
 
 MUON_PLAN_TILED_SMALL = 1
 MUON_PLAN_PIPELINE = 2
+MUON_PLAN_UNFUSED_NORMALIZE = 4
 
 MUON_SCALE_NONE = 0
 MUON_SCALE_ASPECT = 1

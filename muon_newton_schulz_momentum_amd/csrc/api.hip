@@ -35,6 +35,29 @@ muon_status check_step(const muon_plan* p, int32_t chunk, const char* who) {
     return MUON_OK;
 }
 
+// X0 bookkeeping (muon_plan::x0_fresh): a Newton–Schulz call consumes the chunk's X0, and
+// a momentum update of a chunk overwrites the X0 of every other chunk in its region.
+void mark_x0(const muon_plan* p, int32_t chunk, bool fresh) {
+    std::vector<uint8_t>& f = const_cast<muon_plan*>(p)->x0_fresh;
+    const int32_t n = (int32_t)f.size();
+    for (int32_t i = 0; i < n; ++i) {
+        if (chunk != -1 && i != chunk) continue;
+        if (fresh)
+            for (int32_t k = 0; k < n; ++k)
+                if (p->chunks[(size_t)k].region_off == p->chunks[(size_t)i].region_off) f[(size_t)k] = 0;
+        f[(size_t)i] = fresh ? 1 : 0;
+    }
+}
+muon_status check_x0(const muon_plan* p, int32_t chunk, const char* who) {
+    for (int32_t i = 0; i < (int32_t)p->x0_fresh.size(); ++i)
+        if ((chunk == -1 || i == chunk) && !p->x0_fresh[(size_t)i])
+            return set_error(MUON_ERR_INVALID_ARG,
+                             std::string(who) + ": chunk " + std::to_string(i) +
+                                 " holds no fresh X0 (bf16 momentum): an earlier Newton-Schulz call or step has "
+                                 "consumed it, or none was made; call muon_momentum_update first");
+    return MUON_OK;
+}
+
 // ---- per-launch timing ------------------------------------------------------------------
 
 // Set while this thread records a step into a graph: launches then carry no event pairs,
@@ -166,19 +189,30 @@ uint16_t* ns_start(const muon_plan* p, const Chunk& c, int32_t steps) {
     return (steps & 1) ? at<uint16_t>(p, c.off_xq) : at<uint16_t>(p, c.off_xp);
 }
 
+// Whether the chunk's normalisation is fused into the first iteration's operand loads:
+// the 256-tile kernels with an odd iteration count (X0 is then read where the first
+// iteration starts, in xq, and the last iteration ends in xp as the apply expects).
+bool fused_norm(const muon_plan* p, const Chunk& c, int32_t steps) {
+    return c.tile == TILE_256 && (steps & 1) && !(p->flags & MUON_PLAN_UNFUSED_NORMALIZE);
+}
+
 // Step 2 for a chunk: the normaliser from the momentum kernel's partial sums, then
-// X = bf16(X0 / (||X0|| + eps)) into the starting buffer.
+// X = bf16(X0 / (||X0|| + eps)) into the starting buffer (unless the first iteration's
+// loads do that themselves).
 muon_status ns_prep(const muon_plan* p, const Chunk& c, int32_t steps, float eps, hipStream_t s, bool side = false) {
     uint16_t* xq = at<uint16_t>(p, c.off_xq);
     double* inv = at<double>(p, c.off_inv);
     hipError_t e;
     {
-        FinalizeArgs f{at<const double>(p, c.off_part), inv, c.ew_tiles, (double)eps, at<uint32_t>(p, c.off_sched)};
+        const bool fused = fused_norm(p, c, steps);
+        FinalizeArgs f{at<const double>(p, c.off_part), inv, c.ew_tiles, (double)eps, at<uint32_t>(p, c.off_sched),
+                       fused && (c.mp != c.m || c.np != c.n) ? xq : nullptr, c.m, c.n, c.mp, c.np};
         TimedLaunch tl(p, MUON_KERNEL_NORM_FINALIZE, (double)c.count * c.ew_tiles * 8.0, s);
         e = launch_finalize(f, c.count, s);
         tl.done(s);
         if (e != hipSuccess) return hip_fail(e, "norm finalize kernel launch");
     }
+    if (fused_norm(p, c, steps)) return MUON_OK;
     {
         NormalizeArgs n{xq, ns_start(p, c, steps), inv, c.m, c.n, c.mp, c.np, c.count * c.mp * c.np / 8};
         TimedLaunch tl(p, side ? MUON_KERNEL_NORMALIZE_SIDE : MUON_KERNEL_NORMALIZE, (double)c.count * c.m * c.n * 4.0, s);
@@ -209,6 +243,9 @@ muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int
         uint16_t* nxt = (cur == xp) ? xq : xp;
         NsArgs g{};
         g.sched = at<uint32_t>(p, c.off_sched);
+        // the first iteration normalises X0 as it loads it (fused_norm)
+        const bool norm = it == 0 && fused_norm(p, c, steps);
+        g.inv = norm ? at<const double>(p, c.off_inv) : nullptr;
         // A = X X^T
         g.opa = cur; g.opb = cur; g.ep = cur; g.out = am;
         g.stride_a = xs; g.stride_b = xs; g.stride_o = as;
@@ -226,6 +263,7 @@ muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int
         g.stride_a = as; g.stride_b = as; g.stride_o = as;
         g.lda = (int32_t)c.mp; g.ldb = (int32_t)c.mp; g.ldo = (int32_t)c.mp;
         g.K = (int32_t)c.mp; g.alpha = b_; g.gamma = c_;
+        g.inv = nullptr;                                  // B is computed from A only
         {
             TimedLaunch tl(p, MUON_KERNEL_SYRK_POLY, cnt * m * m * (m + 1.0), s);
             e = launch_ns(NS_POLY, tile, g, s);
@@ -238,6 +276,7 @@ muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int
         g.lda = (int32_t)c.mp; g.ldb = (int32_t)c.np; g.ldo = (int32_t)c.np;
         g.K = (int32_t)c.mp; g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn;
         g.total_tiles = (int32_t)(c.count * tm * tn); g.alpha = a_; g.gamma = 1.f;
+        g.inv = norm ? at<const double>(p, c.off_inv) : nullptr;
         {
             TimedLaunch tl(p, MUON_KERNEL_GEMM_AXPY, cnt * 2.0 * m * m * n, s);
             e = launch_ns(NS_AXPY, tile, g, s);
@@ -605,6 +644,7 @@ muon_status muon_plan_bind(muon_plan* p, void* ws, uint64_t bytes, void* stream)
     p->ws = ws;
     p->ws_given = bytes;
     p->bound = true;
+    p->x0_fresh.assign(p->chunks.size(), 0);
     return MUON_OK;
 }
 
@@ -620,6 +660,7 @@ muon_status muon_momentum_update(const muon_plan* p, int32_t chunk, float beta, 
         if (chunk != -1 && i != chunk) continue;
         if ((st = momentum_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
     }
+    mark_x0(p, chunk, true);
     return MUON_OK;
 }
 
@@ -632,7 +673,9 @@ muon_status muon_ns_batched_schedule(const muon_plan* p, int32_t chunk, const fl
     if (steps < 1 || steps > MAX_NS_STEPS)
         return set_error(MUON_ERR_INVALID_ARG, "muon_ns_batched_schedule: steps must be in [1, 1024]");
     if ((st = check_ns(steps, coeffs, eps, "muon_ns_batched_schedule")) != MUON_OK) return st;
+    if ((st = check_x0(p, chunk, "muon_ns_batched_schedule")) != MUON_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_x0(p, chunk, false);
     if (chunk == -1) return ns_all(p, coeffs, steps, eps, s);
     return ns_one(p, chunk, coeffs, steps, eps, s);
 }
@@ -648,7 +691,9 @@ muon_status muon_ns_batched(const muon_plan* p, int32_t chunk, float a, float b,
     cfg.steps = steps;
     fill_abc(cfg, a, b, c);
     if ((st = check_ns(steps, cfg.abc.data(), eps, "muon_ns_batched")) != MUON_OK) return st;
+    if ((st = check_x0(p, chunk, "muon_ns_batched")) != MUON_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    mark_x0(p, chunk, false);
     if (chunk == -1) return ns_all(p, cfg.abc.data(), steps, eps, s);
     return ns_one(p, chunk, cfg.abc.data(), steps, eps, s);
 }
@@ -678,6 +723,7 @@ muon_status muon_step_ex(const muon_plan* p, int32_t chunk, const muon_step_conf
     StepCfg cfg;
     muon_status st = make_cfg(config, cfg, "muon_step_ex");
     if (st != MUON_OK) return st;
+    mark_x0(p, chunk, false);      // the step makes and consumes its own X0
     return step_chunks(p, chunk, cfg, static_cast<hipStream_t>(stream));
 }
 
@@ -722,6 +768,7 @@ muon_status muon_graph_capture_ex(const muon_plan* p, const muon_step_config* co
     t_capturing = true;
     st = step_chunks(p, -1, cfg, cs);
     t_capturing = false;
+    mark_x0(p, -1, false);         // every replay makes and consumes its own X0
     const std::string launch_error = st == MUON_OK ? std::string() : std::string(muon_last_error());
     e = hipStreamEndCapture(cs, &graph);
     (void)hipStreamDestroy(cs);

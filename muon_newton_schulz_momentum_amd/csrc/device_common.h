@@ -29,7 +29,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x
 // in float32 and rounded to bf16 by the packed conversion; elements from `valid` on (the
 // padding past the matrix's last column) are zero.  Every kernel that normalises (one
 // stream, side stream, fused small matrices) uses this, so their results agree bitwise.
-__device__ __forceinline__ uint4 normalize8(uint4 in, int64_t valid, float s) {
+__device__ __forceinline__ uint4 normalize8(uint4 in, int32_t valid, float s) {
     const uint32_t w[4] = {in.x, in.y, in.z, in.w};
     uint32_t o[4];
 #pragma unroll
@@ -39,6 +39,20 @@ __device__ __forceinline__ uint4 normalize8(uint4 in, int64_t valid, float s) {
         o[j] = y;
     }
     return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The same normalisation for 4 values (8 bytes): per element exactly what normalize8 does,
+// so a fused path that normalises the values it loads agrees bitwise with the separate pass.
+__device__ __forceinline__ uint2 normalize4(uint2 in, int32_t valid, float s) {
+    const uint32_t w[2] = {in.x, in.y};
+    uint32_t o[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint32_t y = f32x2_to_bf16x2(__uint_as_float(w[j] << 16) * s, __uint_as_float(w[j] & 0xffff0000u) * s);
+        if (2 * j + 1 >= valid) y &= (2 * j < valid) ? 0x0000ffffu : 0u;
+        o[j] = y;
+    }
+    return make_uint2(o[0], o[1]);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

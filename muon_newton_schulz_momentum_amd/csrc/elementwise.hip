@@ -264,10 +264,31 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
         const double tot = (red[0] + red[1]) + (red[2] + red[3]);
         a.inv[mat] = 1.0 / (sqrt(tot) + a.eps);
     }
+    if (a.x0) {
+        // X0's padding: the rows past m whole, and columns n .. np-1 of the first m rows
+        // (whole 16-byte units from the first multiple of 8 at or past n, single elements
+        // before it)
+        uint16_t* x = a.x0 + mat * a.mp * a.np;
+        const int64_t upr = a.np / 8;                       // 16-byte units per row
+        const int64_t c8 = (a.n + 7) / 8;                   // first unit wholly past n
+        const int64_t tail = c8 * 8 - a.n;                  // single elements before it
+        const int64_t n_rows = (a.mp - a.m) * upr, n_cols = a.m * (upr - c8), n_tail = a.m * tail;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        for (int64_t u = tid; u < n_rows; u += 256)
+            *reinterpret_cast<uint4*>(x + a.m * a.np + u * 8) = z;
+        for (int64_t u = tid; u < n_cols; u += 256) {
+            const int64_t r = u / (upr - c8), k = u - r * (upr - c8);
+            *reinterpret_cast<uint4*>(x + r * a.np + (c8 + k) * 8) = z;
+        }
+        for (int64_t u = tid; u < n_tail; u += 256) {
+            const int64_t r = u / tail, k = u - r * tail;
+            x[r * a.np + a.n + k] = 0;
+        }
+    }
 }
 
 __device__ __forceinline__ uint4 normalize_unit(uint4 in, int64_t c, int64_t n, double s) {
-    return dev::normalize8(in, n - c, (float)s);
+    return dev::normalize8(in, (int32_t)(n - c < 8 ? n - c : 8), (float)s);
 }
 
 // The chunk's matrices are mp x np blocks one after another, so unit u (8 elements) is in

@@ -33,6 +33,10 @@ struct FinalizeArgs {
     // the chunk's tile-queue block, zeroed here before its product launches: in a region
     // shared with other chunks, their data may have overwritten it since its last use
     uint32_t* sched;
+    // nullable: X0 (count matrices of mp x np bf16, valid m x n) whose padding is zeroed
+    // here, for chunks whose first iteration normalises X0 as it loads it
+    uint16_t* x0;
+    int64_t m, n, mp, np;
 };
 
 struct NormalizeArgs {
@@ -85,6 +89,11 @@ struct NsArgs {
     // (the finalize kernel zeroes them before a chunk's first product launch, and each
     // launch's last workgroup sets them back to zero for the next)
     uint32_t* sched;
+    // Normalisation fused into the first iteration's loads (256-tile SYRK and AXPY only):
+    // when set, every X operand value is read as X0 and used as bf16(X0 * f32(inv[matrix]))
+    // (the separate normalize pass's arithmetic); X0's padding must be zero (the finalize
+    // kernel zeroes it for such chunks).
+    const double* inv;
 };
 
 // Whole Newton–Schulz of small matrices (canonical m <= 64, padded n <= SMALL_NS_MAX_N,

@@ -488,9 +488,13 @@ __device__ __forceinline__ void lds_wait_barrier() {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-template <int MODE, int WM, int WN, bool PERSIST>
+// NORM (SYRK and AXPY of the first iteration): the X operand is read as X0 and normalised
+// in the staging registers on its way to LDS (and the AXPY's E tile as it is combined), with
+// the separate normalize pass's arithmetic, so no normalised copy of X is ever written.
+template <int MODE, int WM, int WN, bool PERSIST, bool NORM>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WM * WN / 4, WM * WN / 4)))
 void ns_vs_kernel(NsArgs p) {
+    static_assert(!NORM || MODE != NS_POLY, "only SYRK and AXPY read X");
     constexpr int TILE = 256, BK = 64, NW = WM * WN, NT = 64 * NW;
     constexpr int WTM = TILE / WM, WTN = TILE / WN, FM = WTM / 32, FN = WTN / 32;
     constexpr int RP_ROWS = NT / 8;                   // row-panel rows per staging pass
@@ -542,6 +546,8 @@ void ns_vs_kernel(NsArgs p) {
     if (MODE == NS_AXPY) grid_decode(t, p.tiles_m, p.tiles_n, ti, tj);
     else tri_decode(t, p.tiles_m, ti, tj);
     const bool diag = MODE != NS_AXPY && ti == tj;
+    // the matrix's normaliser (NORM), rounded to float32 as the normalize pass rounds it
+    const float s_norm = NORM ? (float)p.inv[mat] : 1.f;
 
     // buffer resources from the first element of each operand panel to the end of its matrix
     const int64_t a0 = (int64_t)ti * TILE * p.lda;
@@ -578,14 +584,28 @@ void ns_vs_kernel(NsArgs p) {
         else
             sb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_rp, kt * BK * 2 + i * RP_ROWS * p.ldb * 2, 0);
     };
+    // NORM: a staged 16-byte piece of X0 becomes bf16(X0 * s).  The padding outside the
+    // m x n region needs no mask: the finalize kernel has zeroed it in X0.  The scheduling
+    // barriers keep the compiler from spreading the arithmetic over the neighbouring slots
+    // (which costs registers the side-stream kernels need).
+    auto norm16 = [&](i32x4 v) {
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 u = dev::normalize8(__builtin_bit_cast(uint4, v), 8, s_norm);
+        __builtin_amdgcn_sched_barrier(0);
+        return __builtin_bit_cast(i32x4, u);
+    };
     auto swrite_a = [&](int i, int st) {
-        *reinterpret_cast<i32x4*>(smem + w_rp + st * RP_B + i * RP_ROWS * 32) = sa[i];
+        i32x4 v = sa[i];
+        if (NORM && MODE == NS_SYRK) v = norm16(v);
+        *reinterpret_cast<i32x4*>(smem + w_rp + st * RP_B + i * RP_ROWS * 32) = v;
     };
     auto swrite_b = [&](int i, int st) {
+        i32x4 v = sb[i];
+        if (NORM) v = norm16(v);
         if (MODE == NS_AXPY)
-            *reinterpret_cast<i32x4*>(smem + w_kn[i & 1] + st * KN_B + i * KN_ROWS * TILE * 2) = sb[i];
+            *reinterpret_cast<i32x4*>(smem + w_kn[i & 1] + st * KN_B + i * KN_ROWS * TILE * 2) = v;
         else
-            *reinterpret_cast<i32x4*>(smem + OFF_B + w_rp + st * RP_B + i * RP_ROWS * 32) = sb[i];
+            *reinterpret_cast<i32x4*>(smem + OFF_B + w_rp + st * RP_B + i * RP_ROWS * 32) = v;
     };
 
     f32x16 acc[FM][FN];
@@ -752,7 +772,8 @@ void ns_vs_kernel(NsArgs p) {
 #pragma unroll
                 for (int w = 0; w < 4; ++w) v[w] = acc[i][j][4 * q + w];
                 if (MODE == NS_POLY || MODE == NS_AXPY) {
-                    const uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
+                    uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
+                    if (NORM) e = dev::normalize4(e, 8, s_norm);
                     const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
 #pragma unroll
                     for (int w = 0; w < 4; ++w) v[w] = dev::ns_combine(p.alpha, __builtin_bit_cast(float, ew[w]), p.gamma, v[w]);
@@ -857,19 +878,34 @@ hipError_t launch_cfg(const NsArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int MODE, bool NORM>
+void launch_vs(const NsArgs& a, hipStream_t s) {
+    if (a.total_tiles >= 2 * PERSIST_GRID)
+        hipLaunchKernelGGL((ns_vs_kernel<MODE, VS_WM, VS_WN, true, NORM>), dim3((unsigned)PERSIST_GRID),
+                           dim3(64 * VS_WM * VS_WN), 0, s, a);
+    else
+        hipLaunchKernelGGL((ns_vs_kernel<MODE, VS_WM, VS_WN, false, NORM>), dim3((unsigned)a.total_tiles),
+                           dim3(64 * VS_WM * VS_WN), 0, s, a);
+}
+
 template <int MODE>
 hipError_t launch_mode(int32_t tile, const NsArgs& a, hipStream_t s) {
     switch (tile) {
         case TILE_256:
-            if (a.total_tiles >= 2 * PERSIST_GRID)
-                hipLaunchKernelGGL((ns_vs_kernel<MODE, VS_WM, VS_WN, true>), dim3((unsigned)PERSIST_GRID),
-                                   dim3(64 * VS_WM * VS_WN), 0, s, a);
-            else
-                hipLaunchKernelGGL((ns_vs_kernel<MODE, VS_WM, VS_WN, false>), dim3((unsigned)a.total_tiles),
-                                   dim3(64 * VS_WM * VS_WN), 0, s, a);
+            if constexpr (MODE != NS_POLY) {
+                if (a.inv) launch_vs<MODE, true>(a, s);
+                else launch_vs<MODE, false>(a, s);
+            } else {
+                if (a.inv) return hipErrorInvalidValue;
+                launch_vs<MODE, false>(a, s);
+            }
             return hipGetLastError();
-        case TILE_128: return launch_cfg<MODE, 128, 2, 2, 64, 2>(a, s);
-        case TILE_64: return launch_cfg<MODE, 64, 2, 2, 64, 2>(a, s);
+        case TILE_128:
+            if (a.inv) return hipErrorInvalidValue;   // the direct-to-LDS tiles do not normalise
+            return launch_cfg<MODE, 128, 2, 2, 64, 2>(a, s);
+        case TILE_64:
+            if (a.inv) return hipErrorInvalidValue;
+            return launch_cfg<MODE, 64, 2, 2, 64, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

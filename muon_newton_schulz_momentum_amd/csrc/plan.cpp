@@ -171,7 +171,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (scale_mode != MUON_SCALE_NONE && scale_mode != MUON_SCALE_ASPECT && scale_mode != MUON_SCALE_RMS_MATCH)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown scale_mode");
     const uint32_t flags = opts ? opts->flags : 0u;
-    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_PIPELINE)) != 0)
+    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_PIPELINE | MUON_PLAN_UNFUSED_NORMALIZE)) != 0)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown flag bits");
 
     // ---- validate every descriptor -----------------------------------------------------

@@ -109,6 +109,10 @@ struct muon_plan {
     // the two-stream pipeline: a second stream and its ordering events, created at bind
     void* side = nullptr;                 // hipStream_t
     std::vector<void*> pipe_events;       // hipEvent_t, timing disabled
+    // per chunk, in the order calls were enqueued: 1 when the workspace holds a fresh X0 =
+    // bf16(M) from muon_momentum_update that no Newton–Schulz call has consumed yet (the
+    // iterations overwrite X0 with their ping-pong buffers)
+    std::vector<uint8_t> x0_fresh;
 };
 
 // An instantiated graph of one whole step.  It holds the device addresses of the

@@ -50,7 +50,8 @@ def test_side_kernels_fit_beside_a_product_workgroup():
     ns = _resources("ns_gemm.hip")
     gemm = [r for k, r in ns.items() if "ns_vs_kernel" in k]
     side = {k: r for k, r in ew.items() if "_side_kernel" in k}
-    assert len(gemm) == 6 and len(side) == 4, (sorted(ns), sorted(ew))   # 3 modes x (one tile, persistent)
+    # 3 modes x (one tile, persistent), plus SYRK and AXPY with the fused normalisation
+    assert len(gemm) == 10 and len(side) == 4, (sorted(ns), sorted(ew))
     g_regs = max(_alloc(r) for r in gemm)
     g_lds = max(r["LDS"] for r in gemm)
     for k, r in side.items():
