@@ -366,6 +366,28 @@ MUON_API muon_status muon_graph_node_count(const muon_graph* graph, int64_t* nod
 /* Free the graph; the caller makes sure no launch of it is still running. */
 MUON_API void muon_graph_destroy(muon_graph* graph);
 
+/* ---- a step that allocates nothing ------------------------------------------------------ */
+
+/* Bytes of the library's own static device scratch (one copy per GPU, held until the
+ * process ends). */
+#define MUON_NOALLOC_MAX_BYTES (64ull << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): muon_step_ex for every chunk, on one
+ * stream, with the library's static scratch array on the current device as the workspace
+ * instead of a bound one.  The plan need not be bound; it must need at most
+ * MUON_NOALLOC_MAX_BYTES of workspace (muon_plan_workspace_bytes).  Each call clears the
+ * part of the scratch the plan uses (with a kernel) and copies the plan's tables into it
+ * (hipMemcpyAsync from the plan's host memory, which the plan owns), then runs the step;
+ * config->pipeline is ignored (one stream).  Calls no hipMalloc or hipFree.  Every call
+ * on one GPU shares that GPU's scratch and leaves its contents there: calls that overlap
+ * on one GPU (different streams or threads) race, and the result O cannot be read back
+ * (muon_plan_param_info refers to a bound workspace).  The first call on a device looks
+ * the scratch's address up on that device.
+ * Errors: INVALID_ARG (NULL plan, config as for muon_step_ex), WORKSPACE_TOO_SMALL (the
+ * plan needs more than MUON_NOALLOC_MAX_BYTES), SHAPE, HIP. */
+MUON_API muon_status muon_step_noalloc(const muon_plan* plan, const muon_step_config* config, void* stream);
+
 /* ---- per-kernel timing (HIP events on the launching stream) --------------------------- */
 
 #define MUON_KERNEL_MOMENTUM 0

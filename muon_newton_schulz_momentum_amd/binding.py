@@ -132,6 +132,8 @@ muon_ns_batched_schedule = _fn("muon_ns_batched_schedule", C.c_int32,
 muon_adamw_step = _fn("muon_adamw_step", C.c_int32, [_P, C.POINTER(muon_adamw_config), C.c_void_p])
 muon_plan_adamw_counts = _fn("muon_plan_adamw_counts", C.c_int32, [_P, C.POINTER(C.c_int64), C.POINTER(C.c_int64)])
 muon_step_ex = _fn("muon_step_ex", C.c_int32, [_P, C.c_int32, C.POINTER(muon_step_config), C.c_void_p])
+muon_step_noalloc = _fn("muon_step_noalloc", C.c_int32, [_P, C.POINTER(muon_step_config), C.c_void_p])
+MUON_NOALLOC_MAX_BYTES = 64 << 20
 muon_step = _fn("muon_step", C.c_int32,
                 [_P, C.c_int32, C.c_float, C.c_float, C.c_float, C.c_float, C.c_int32, C.c_float,
                  C.c_float, C.c_float, C.c_void_p])
@@ -156,7 +158,7 @@ EXPORTED = [
     "muon_plan_buckets", "muon_plan_workspace_bytes", "muon_plan_counts", "muon_plan_info",
     "muon_plan_param_info", "muon_plan_validate", "muon_plan_bind", "muon_momentum_update",
     "muon_ns_batched", "muon_ns_batched_schedule", "muon_apply", "muon_adamw_step", "muon_plan_adamw_counts",
-    "muon_step", "muon_step_ex",
+    "muon_step", "muon_step_ex", "muon_step_noalloc",
     "muon_graph_capture", "muon_graph_capture_ex", "muon_graph_launch",
     "muon_graph_node_count", "muon_graph_destroy", "muon_timing_enable", "muon_timing_read",
     "muon_timing_reset", "muon_kernel_name", "muon_plan_destroy", "muon_status_string",

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -583,6 +584,39 @@ bool grid_fits(const Chunk& c) {
            c.mp * c.mp * 2 < lim && c.count * c.mp < lim;
 }
 
+// ---- the library's static scratch (muon_step_noalloc) -------------------------------------
+
+constexpr uint64_t NOALLOC_BYTES = MUON_NOALLOC_MAX_BYTES;
+static_assert(NOALLOC_BYTES % 16 == 0, "scratch is cleared in 16-byte units");
+
+// One copy per GPU, in the code object's device memory.  Host code must not pass the
+// array's name to a kernel (on the host it is only a handle for the runtime); it uses the
+// device address looked up per device below.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[NOALLOC_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The scratch's device address on the current device, looked up on the first call there.
+muon_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "muon_step_noalloc: hipGetDevice");
+    if (dev < 0 || dev >= MAX_DEVICES) return set_error(MUON_ERR_INVALID_ARG, "muon_step_noalloc: device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "muon_step_noalloc: hipGetSymbolAddress(scratch)");
+        if (!ptr || ((uintptr_t)ptr & (WS_ALIGN - 1)) != 0)
+            return set_error(MUON_ERR_HIP, "muon_step_noalloc: the scratch's device address is not 256-byte aligned");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -735,6 +769,48 @@ muon_status muon_adamw_step(const muon_plan* p, const muon_adamw_config* config,
     muon_status st = make_adam(config, a, "muon_adamw_step");
     if (st != MUON_OK) return st;
     return adam_run(p, a, static_cast<hipStream_t>(stream));
+}
+
+muon_status muon_step_noalloc(const muon_plan* p, const muon_step_config* config, void* stream) {
+    clear_error();
+    if (!p) return set_error(MUON_ERR_INVALID_ARG, "muon_step_noalloc: plan is NULL");
+    StepCfg cfg;
+    muon_status st = make_cfg(config, cfg, "muon_step_noalloc");
+    if (st != MUON_OK) return st;
+    cfg.pipeline = false;
+    if (p->ws_bytes > NOALLOC_BYTES)
+        return set_error(MUON_ERR_WORKSPACE_TOO_SMALL, "muon_step_noalloc: the plan needs " +
+                                                           std::to_string(p->ws_bytes) + " bytes of workspace; the static scratch holds " +
+                                                           std::to_string(NOALLOC_BYTES));
+    for (const Chunk& c : p->chunks)
+        if (!grid_fits(c)) return set_error(MUON_ERR_SHAPE, "muon_step_noalloc: chunk tile grid too large");
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != MUON_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the previous call's contents go: clear what this plan uses, then its tables
+    hipError_t e = launch_zero(ws, (p->ws_bytes + 15) / 16, s);
+    if (e != hipSuccess) return hip_fail(e, "muon_step_noalloc: clear kernel launch");
+    if (!p->adam.empty()) {
+        e = hipMemcpyAsync(static_cast<char*>(ws) + p->off_adam, p->adam.data(), p->adam.size() * sizeof(AdamEntry),
+                           hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(static_cast<char*>(ws) + p->off_adam_segs, p->adam_segs.data(),
+                               p->adam_segs.size() * sizeof(AdamSeg), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "muon_step_noalloc: AdamW table copy");
+    }
+    if (!p->table.empty()) {
+        e = hipMemcpyAsync(ws, p->table.data(), p->table.size() * sizeof(MatEntry), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "muon_step_noalloc: table copy");
+    }
+    // the step's kernels take their addresses from the plan's workspace base: point it at
+    // the scratch for the launches (calls on one plan do not overlap), then restore it
+    muon_plan* mp = const_cast<muon_plan*>(p);
+    void* const saved = mp->ws;
+    mp->ws = ws;
+    st = step_chunks(mp, -1, cfg, s);
+    mp->ws = saved;
+    mark_x0(p, -1, false);
+    return st;
 }
 
 muon_status muon_step(const muon_plan* p, int32_t chunk, float beta, float a, float b, float c, int32_t steps,

@@ -11,6 +11,8 @@
 // Bitwise agreement with the float64 oracle: the momentum and apply arithmetic is done
 // in float64 with each product and sum rounded as written (contraction is off in this
 // file), then rounded once to float32; bf16 casts round to nearest even.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -955,6 +957,18 @@ hipError_t launch_momentum(const MomentumArgs& a, int32_t grad_dtype, hipStream_
         hipLaunchKernelGGL(momentum_kernel<MUON_DTYPE_F32>, dim3(grid), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(momentum_kernel<MUON_DTYPE_BF16>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint4* dst, uint64_t units) {
+    for (uint64_t u = (uint64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (uint64_t)gridDim.x * 256)
+        dst[u] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero(void* dst, uint64_t units, hipStream_t s) {
+    if (units == 0) return hipSuccess;
+    const uint64_t blocks = std::min<uint64_t>((units + 255) / 256, 2048);
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<uint4*>(dst), units);
     return hipGetLastError();
 }
 

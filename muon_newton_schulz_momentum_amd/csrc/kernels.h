@@ -131,5 +131,7 @@ hipError_t launch_normalize_side(const NormalizeArgs& a, hipStream_t s);
 hipError_t launch_apply_side(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_small(const SmallNsArgs& a, int64_t total, hipStream_t s);
+// Zero `units` 16-byte units at `dst` (a kernel, so it may sit in a captured graph).
+hipError_t launch_zero(void* dst, uint64_t units, hipStream_t s);
 
 }  // namespace muon

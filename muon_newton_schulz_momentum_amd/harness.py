@@ -194,6 +194,13 @@ class Plan:
         L.check(L.muon_step_ex(self._plan, chunk, C.byref(k), _stream_ptr(stream)), "muon_step_ex")
         del keep
 
+    def step_noalloc(self, beta, lr, wd, stream=None, **kw):
+        """The whole step on one stream with libmuon's static scratch as the workspace
+        (muon_step_noalloc; the plan need not be bound)."""
+        k, keep = self.config(beta, lr, wd, **kw)
+        L.check(L.muon_step_noalloc(self._plan, C.byref(k), _stream_ptr(stream)), "muon_step_noalloc")
+        del keep
+
     def capture_ex(self, beta, lr, wd, **kw) -> "Graph":
         k, keep = self.config(beta, lr, wd, **kw)
         g = C.c_void_p()
