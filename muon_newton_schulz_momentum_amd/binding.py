@@ -48,7 +48,9 @@ MUON_KERNEL_ADAMW = 8
 MUON_KERNEL_MOMENTUM_SIDE = 9
 MUON_KERNEL_NORMALIZE_SIDE = 10
 MUON_KERNEL_APPLY_SIDE = 11
-MUON_KERNEL_COUNT = 12
+MUON_KERNEL_NS_GROUPED = 12
+MUON_KERNEL_PREP_GROUPED = 13
+MUON_KERNEL_COUNT = 14
 
 MUON_OPT_DEFAULT = 0
 MUON_OPT_ADAMW = 1
@@ -57,6 +59,7 @@ MUON_OPT_NONE = 2
 MUON_PLAN_TILED_SMALL = 1
 MUON_PLAN_PIPELINE = 2
 MUON_PLAN_UNFUSED_NORMALIZE = 4
+MUON_PLAN_UNGROUPED = 8
 
 MUON_SCALE_NONE = 0
 MUON_SCALE_ASPECT = 1
@@ -84,7 +87,7 @@ class muon_chunk_info(C.Structure):
     _fields_ = [("m", C.c_int64), ("n", C.c_int64), ("m_pad", C.c_int64), ("n_pad", C.c_int64),
                 ("count", C.c_int64), ("bucket", C.c_int32), ("tile", C.c_int32),
                 ("grad_dtype", C.c_int32), ("shared_region", C.c_int32),
-                ("fused_small", C.c_int32), ("reserved", C.c_int32),
+                ("fused_small", C.c_int32), ("grouped_small", C.c_int32),
                 ("flops_conventional", C.c_double), ("flops_algorithmic", C.c_double),
                 ("bytes_momentum", C.c_double), ("bytes_apply", C.c_double),
                 ("region_offset", C.c_uint64), ("region_bytes", C.c_uint64)]

@@ -44,8 +44,12 @@ void mark_x0(const muon_plan* p, int32_t chunk, bool fresh) {
     for (int32_t i = 0; i < n; ++i) {
         if (chunk != -1 && i != chunk) continue;
         if (fresh)
-            for (int32_t k = 0; k < n; ++k)
-                if (p->chunks[(size_t)k].region_off == p->chunks[(size_t)i].region_off) f[(size_t)k] = 0;
+            for (int32_t k = 0; k < n; ++k) {
+                const Chunk& a = p->chunks[(size_t)k];
+                const Chunk& b = p->chunks[(size_t)i];
+                if (a.region_off < b.region_off + b.region_bytes && b.region_off < a.region_off + a.region_bytes)
+                    f[(size_t)k] = 0;
+            }
         f[(size_t)i] = fresh ? 1 : 0;
     }
 }
@@ -224,69 +228,160 @@ muon_status ns_prep(const muon_plan* p, const Chunk& c, int32_t steps, float eps
     return MUON_OK;
 }
 
-// Step 3 for a chunk: the iterations, from the normalised X.
-muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, hipStream_t s) {
-    uint16_t* xp = at<uint16_t>(p, c.off_xp);
-    uint16_t* xq = at<uint16_t>(p, c.off_xq);
+// The arguments of one product launch over chunk c, X read from `cur`, X' written to `nxt`
+// (the same for the chunk's own launches and for the grouped ones).  `norm`: the first
+// iteration of a fused_norm chunk.
+NsArgs ns_args(const muon_plan* p, const Chunk& c, NsMode mode, uint16_t* cur, uint16_t* nxt, float alpha,
+               float gamma, bool norm) {
     uint16_t* am = at<uint16_t>(p, c.off_a);
     uint16_t* bm = at<uint16_t>(p, c.off_b);
-    uint16_t* cur = ns_start(p, c, steps);
-    hipError_t e;
-
-    const int32_t tile = c.tile;
-    const int32_t tm = (int32_t)(c.mp / tile), tn = (int32_t)(c.np / tile);
+    const int32_t tm = (int32_t)(c.mp / c.tile), tn = (int32_t)(c.np / c.tile);
     const int32_t tri = tm * (tm + 1) / 2;
     const int64_t xs = c.mp * c.np, as = c.mp * c.mp;
-    const double m = (double)c.m, n = (double)c.n, cnt = (double)c.count;
-
-    for (int32_t it = 0; it < steps; ++it) {
-        const float a_ = abc[3 * it], b_ = abc[3 * it + 1], c_ = abc[3 * it + 2];
-        uint16_t* nxt = (cur == xp) ? xq : xp;
-        NsArgs g{};
-        g.sched = at<uint32_t>(p, c.off_sched);
-        // the first iteration normalises X0 as it loads it (fused_norm)
-        const bool norm = it == 0 && fused_norm(p, c, steps);
-        g.inv = norm ? at<const double>(p, c.off_inv) : nullptr;
-        // A = X X^T
+    NsArgs g{};
+    g.sched = at<uint32_t>(p, c.off_sched);
+    g.alpha = alpha;
+    g.gamma = gamma;
+    if (mode == NS_SYRK) {              // A = X X^T
         g.opa = cur; g.opb = cur; g.ep = cur; g.out = am;
         g.stride_a = xs; g.stride_b = xs; g.stride_o = as;
         g.lda = (int32_t)c.np; g.ldb = (int32_t)c.np; g.ldo = (int32_t)c.mp;
         g.K = (int32_t)c.np; g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tri;
-        g.total_tiles = (int32_t)(c.count * tri); g.alpha = 0.f; g.gamma = 1.f;
-        {
-            TimedLaunch tl(p, MUON_KERNEL_SYRK, cnt * m * (m + 1.0) * n, s);
-            e = launch_ns(NS_SYRK, tile, g, s);
-            tl.done(s);
-            if (e != hipSuccess) return hip_fail(e, "SYRK kernel launch");
-        }
-        // B = b A + c A A^T
+        g.total_tiles = (int32_t)(c.count * tri);
+        g.inv = norm ? at<const double>(p, c.off_inv) : nullptr;
+    } else if (mode == NS_POLY) {       // B = b A + c A A^T (B is computed from A only)
         g.opa = am; g.opb = am; g.ep = am; g.out = bm;
         g.stride_a = as; g.stride_b = as; g.stride_o = as;
         g.lda = (int32_t)c.mp; g.ldb = (int32_t)c.mp; g.ldo = (int32_t)c.mp;
-        g.K = (int32_t)c.mp; g.alpha = b_; g.gamma = c_;
-        g.inv = nullptr;                                  // B is computed from A only
-        {
-            TimedLaunch tl(p, MUON_KERNEL_SYRK_POLY, cnt * m * m * (m + 1.0), s);
-            e = launch_ns(NS_POLY, tile, g, s);
-            tl.done(s);
-            if (e != hipSuccess) return hip_fail(e, "SYRK+poly kernel launch");
-        }
-        // X' = a X + B X
+        g.K = (int32_t)c.mp; g.tiles_m = tm; g.tiles_n = tm; g.tiles_per_mat = tri;
+        g.total_tiles = (int32_t)(c.count * tri);
+    } else {                            // X' = a X + B X
         g.opa = bm; g.opb = cur; g.ep = cur; g.out = nxt;
         g.stride_a = as; g.stride_b = xs; g.stride_o = xs;
         g.lda = (int32_t)c.mp; g.ldb = (int32_t)c.np; g.ldo = (int32_t)c.np;
         g.K = (int32_t)c.mp; g.tiles_m = tm; g.tiles_n = tn; g.tiles_per_mat = tm * tn;
-        g.total_tiles = (int32_t)(c.count * tm * tn); g.alpha = a_; g.gamma = 1.f;
+        g.total_tiles = (int32_t)(c.count * tm * tn);
         g.inv = norm ? at<const double>(p, c.off_inv) : nullptr;
-        {
-            TimedLaunch tl(p, MUON_KERNEL_GEMM_AXPY, cnt * 2.0 * m * m * n, s);
-            e = launch_ns(NS_AXPY, tile, g, s);
+    }
+    return g;
+}
+
+// Algorithmic FLOPs of one product launch over chunk c.
+double mode_flops(const Chunk& c, NsMode mode) {
+    const double m = (double)c.m, n = (double)c.n, cnt = (double)c.count;
+    return mode == NS_SYRK ? cnt * m * (m + 1.0) * n : mode == NS_POLY ? cnt * m * m * (m + 1.0) : cnt * 2.0 * m * m * n;
+}
+
+const char* mode_name(NsMode mode) {
+    return mode == NS_SYRK ? "SYRK kernel launch" : mode == NS_POLY ? "SYRK+poly kernel launch" : "GEMM+axpy kernel launch";
+}
+
+// Step 3 for a chunk: the iterations, from the normalised X.
+muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, hipStream_t s) {
+    uint16_t* xp = at<uint16_t>(p, c.off_xp);
+    uint16_t* xq = at<uint16_t>(p, c.off_xq);
+    uint16_t* cur = ns_start(p, c, steps);
+    static const int32_t kinds[3] = {MUON_KERNEL_SYRK, MUON_KERNEL_SYRK_POLY, MUON_KERNEL_GEMM_AXPY};
+    for (int32_t it = 0; it < steps; ++it) {
+        const float a_ = abc[3 * it], b_ = abc[3 * it + 1], c_ = abc[3 * it + 2];
+        uint16_t* nxt = (cur == xp) ? xq : xp;
+        // the first iteration normalises X0 as it loads it (fused_norm)
+        const bool norm = it == 0 && fused_norm(p, c, steps);
+        const float alpha[3] = {0.f, b_, a_}, gamma[3] = {1.f, c_, 1.f};
+        for (int32_t k = 0; k < 3; ++k) {
+            const NsMode mode = (NsMode)k;
+            const NsArgs g = ns_args(p, c, mode, cur, nxt, alpha[k], gamma[k], norm);
+            TimedLaunch tl(p, kinds[k], mode_flops(c, mode), s);
+            const hipError_t e = launch_ns(mode, c.tile, g, s);
             tl.done(s);
-            if (e != hipSuccess) return hip_fail(e, "GEMM+axpy kernel launch");
+            if (e != hipSuccess) return hip_fail(e, mode_name(mode));
         }
         cur = nxt;
     }
     return MUON_OK;
+}
+
+// ---- the grouped small tiled chunks ----------------------------------------------------------
+
+std::vector<int32_t> grouped_chunks(const muon_plan* p) {
+    std::vector<int32_t> g;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
+        if (p->chunks[(size_t)i].grouped) g.push_back(i);
+    return g;
+}
+
+// Step 2 for grouped chunks: one launch (per PREP_MAX_JOBS chunks) computes every matrix's
+// normaliser and normalises it into its starting buffer.
+muon_status prep_group(const muon_plan* p, const std::vector<int32_t>& idx, int32_t steps, float eps,
+                       hipStream_t s) {
+    for (size_t g0 = 0; g0 < idx.size(); g0 += PREP_MAX_JOBS) {
+        PrepGroupArgs A{};
+        A.eps = (double)eps;
+        double bytes = 0.0;
+        for (size_t k = g0; k < idx.size() && k < g0 + PREP_MAX_JOBS; ++k) {
+            const Chunk& c = p->chunks[(size_t)idx[k]];
+            PrepJob& J = A.job[A.n_jobs++];
+            J.partials = at<const double>(p, c.off_part);
+            J.src = at<const uint16_t>(p, c.off_xq);
+            J.dst = ns_start(p, c, steps);
+            J.ew_tiles = c.ew_tiles;
+            J.m = c.m; J.n = c.n; J.mp = c.mp; J.np = c.np;
+            J.blocks = ceil_div(c.mp * c.np / 8, 4096);
+            J.first = A.total_blocks;
+            A.total_blocks += c.count * J.blocks;
+            bytes += (double)c.count * ((double)c.m * c.n * 4.0 + (double)c.ew_tiles * 8.0);
+        }
+        TimedLaunch tl(p, MUON_KERNEL_PREP_GROUPED, bytes, s);
+        const hipError_t e = launch_prep_grouped(A, s);
+        tl.done(s);
+        if (e != hipSuccess) return hip_fail(e, "grouped normalisation kernel launch");
+    }
+    return MUON_OK;
+}
+
+// Step 3 for grouped chunks: per iteration one launch per product (per GROUPED_MAX_JOBS
+// chunks) over a single queue of all their tiles.
+muon_status iterate_group(const muon_plan* p, const std::vector<int32_t>& idx, const float* abc, int32_t steps,
+                          hipStream_t s) {
+    std::vector<uint16_t*> cur(idx.size());
+    for (size_t k = 0; k < idx.size(); ++k) cur[k] = ns_start(p, p->chunks[(size_t)idx[k]], steps);
+    for (int32_t it = 0; it < steps; ++it) {
+        const float a_ = abc[3 * it], b_ = abc[3 * it + 1], c_ = abc[3 * it + 2];
+        const float alpha[3] = {0.f, b_, a_}, gamma[3] = {1.f, c_, 1.f};
+        for (int32_t kk = 0; kk < 3; ++kk) {
+            const NsMode mode = (NsMode)kk;
+            for (size_t g0 = 0; g0 < idx.size(); g0 += GROUPED_MAX_JOBS) {
+                GroupedNsArgs G{};
+                double work = 0.0;
+                for (size_t k = g0; k < idx.size() && k < g0 + GROUPED_MAX_JOBS; ++k) {
+                    const Chunk& c = p->chunks[(size_t)idx[k]];
+                    uint16_t* nxt = cur[k] == at<uint16_t>(p, c.off_xp) ? at<uint16_t>(p, c.off_xq) : at<uint16_t>(p, c.off_xp);
+                    GroupedJob& J = G.job[G.n_jobs++];
+                    J.a = ns_args(p, c, mode, cur[k], nxt, alpha[kk], gamma[kk], false);
+                    J.tile = c.tile;
+                    J.first = G.total_tiles;
+                    G.total_tiles += J.a.total_tiles;
+                    work += mode_flops(c, mode);
+                }
+                TimedLaunch tl(p, MUON_KERNEL_NS_GROUPED, work, s);
+                const hipError_t e = launch_ns_grouped(mode, G, s);
+                tl.done(s);
+                if (e != hipSuccess) return hip_fail(e, "grouped product kernel launch");
+            }
+        }
+        for (size_t k = 0; k < idx.size(); ++k) {
+            const Chunk& c = p->chunks[(size_t)idx[k]];
+            cur[k] = cur[k] == at<uint16_t>(p, c.off_xp) ? at<uint16_t>(p, c.off_xq) : at<uint16_t>(p, c.off_xp);
+        }
+    }
+    return MUON_OK;
+}
+
+muon_status ns_group(const muon_plan* p, const std::vector<int32_t>& idx, const float* abc, int32_t steps, float eps,
+                     hipStream_t s) {
+    if (idx.empty()) return MUON_OK;
+    const muon_status st = prep_group(p, idx, steps, eps, s);
+    return st != MUON_OK ? st : iterate_group(p, idx, abc, steps, s);
 }
 
 muon_status ns_chunk(const muon_plan* p, const Chunk& c, const float* abc, int32_t steps, float eps,
@@ -344,20 +439,22 @@ muon_status ns_small_chunks(const muon_plan* p, const std::vector<int32_t>& idx,
 muon_status ns_one(const muon_plan* p, int32_t i, const float* abc, int32_t steps, float eps, hipStream_t s) {
     const Chunk& ch = p->chunks[(size_t)i];
     if (ch.fused) return ns_small_chunks(p, std::vector<int32_t>{i}, abc, steps, eps, s);
+    if (ch.grouped) return ns_group(p, std::vector<int32_t>{i}, abc, steps, eps, s);
     return ns_chunk(p, ch, abc, steps, eps, s);
 }
 
 // Newton–Schulz for every chunk (their regions are distinct): all fused chunks in grouped
-// launches, then the tiled ones.
+// launches, all small tiled chunks in the grouped product launches, then the rest.
 muon_status ns_all(const muon_plan* p, const float* abc, int32_t steps, float eps, hipStream_t s) {
     std::vector<int32_t> small;
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
         if (p->chunks[(size_t)i].fused) small.push_back(i);
     muon_status st = ns_small_chunks(p, small, abc, steps, eps, s);
     if (st != MUON_OK) return st;
+    if ((st = ns_group(p, grouped_chunks(p), abc, steps, eps, s)) != MUON_OK) return st;
     for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
         const Chunk& ch = p->chunks[(size_t)i];
-        if (!ch.fused && (st = ns_chunk(p, ch, abc, steps, eps, s)) != MUON_OK) return st;
+        if (!ch.fused && !ch.grouped && (st = ns_chunk(p, ch, abc, steps, eps, s)) != MUON_OK) return st;
     }
     return MUON_OK;
 }
@@ -389,15 +486,35 @@ hipError_t wait(const muon_plan* p, size_t k, hipStream_t s) {
     return hipStreamWaitEvent(s, (hipEvent_t)p->pipe_events[k], 0);
 }
 
-// The tiled chunks, in plan order, when the two-stream pipeline can run them: at least two,
-// and no two consecutive ones in the same workspace region.  Empty otherwise.
-std::vector<int32_t> pipeline_chunks(const muon_plan* p) {
-    std::vector<int32_t> t;
-    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i)
-        if (!p->chunks[(size_t)i].fused) t.push_back(i);
+// A unit of the two-stream step: one tiled chunk, or every grouped small chunk together.
+using Unit = std::vector<int32_t>;
+
+bool same_region(const muon_plan* p, const Unit& a, const Unit& b) {
+    for (int32_t i : a)
+        for (int32_t k : b)
+            if (p->chunks[(size_t)i].region_base == p->chunks[(size_t)k].region_base) return true;
+    return false;
+}
+
+// The tiled units, in plan order (the group where its first chunk is), when the two-stream
+// pipeline can run them: at least two, and no two consecutive ones in the same workspace
+// region.  Empty otherwise.
+std::vector<Unit> pipeline_units(const muon_plan* p) {
+    std::vector<Unit> t;
+    bool group_done = false;
+    for (int32_t i = 0; i < (int32_t)p->chunks.size(); ++i) {
+        const Chunk& c = p->chunks[(size_t)i];
+        if (c.fused) continue;
+        if (c.grouped) {
+            if (!group_done) t.push_back(grouped_chunks(p));
+            group_done = true;
+            continue;
+        }
+        t.push_back(Unit{i});
+    }
     if (t.size() < 2 || !p->side || p->pipe_events.size() < 1 + 4 * t.size()) return {};
     for (size_t j = 1; j < t.size(); ++j)
-        if (p->chunks[(size_t)t[j]].region_off == p->chunks[(size_t)t[j - 1]].region_off) return {};
+        if (same_region(p, t[j], t[j - 1])) return {};
     return t;
 }
 
@@ -408,34 +525,58 @@ double est_prep_s(const Chunk& c) {         // momentum + normalise bytes, side 
 }
 double est_apply_s(const Chunk& c) { return (double)c.count * c.m * c.n * APPLY_BYTES_PER_ELEM / EST_SIDE_BW; }
 
+// A unit's steps: momentum of each chunk; the normalisation (grouped: one launch); the
+// iterations (grouped: the grouped launches); the apply of each chunk.
+muon_status unit_momentum(const muon_plan* p, const Unit& u, const StepCfg& cfg, hipStream_t s, bool side) {
+    for (int32_t i : u) {
+        const muon_status st = momentum_chunk(p, p->chunks[(size_t)i], cfg, s, side);
+        if (st != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+muon_status unit_prep(const muon_plan* p, const Unit& u, const StepCfg& cfg, hipStream_t s, bool side) {
+    if (p->chunks[(size_t)u[0]].grouped) return prep_group(p, u, cfg.steps, cfg.eps, s);
+    return ns_prep(p, p->chunks[(size_t)u[0]], cfg.steps, cfg.eps, s, side);
+}
+muon_status unit_iterate(const muon_plan* p, const Unit& u, const StepCfg& cfg, hipStream_t s) {
+    if (p->chunks[(size_t)u[0]].grouped) return iterate_group(p, u, cfg.abc.data(), cfg.steps, s);
+    return ns_iterate(p, p->chunks[(size_t)u[0]], cfg.abc.data(), cfg.steps, s);
+}
+muon_status unit_apply(const muon_plan* p, const Unit& u, const StepCfg& cfg, hipStream_t s, bool side) {
+    for (int32_t i : u) {
+        const muon_status st = apply_chunk(p, p->chunks[(size_t)i], cfg, s, side);
+        if (st != MUON_OK) return st;
+    }
+    return MUON_OK;
+}
+
 // The whole step with two streams.  The pages overlap the exchange of the next batch of
 // matrices with the orthogonalisation of the current one ("Frontier Pre-training at
 // Microsoft AI", method details section 5, "Scaling Muon to 16K GPUs", the prefetching of
 // the next batch).  On one GPU the work beside the products is the HBM-bound part of the
-// step: while chunk j's Newton–Schulz products run on the caller's stream s, chunk j+1's
-// momentum and normaliser (P_{j+1}) and chunk j-1's apply (A_{j-1}) run on the plan's side
+// step: while unit j's Newton–Schulz products run on the caller's stream s, unit j+1's
+// momentum and normaliser (P_{j+1}) and unit j-1's apply (A_{j-1}) run on the plan's side
 // stream d, in the side-stream kernels sized to share each compute unit with a product
 // workgroup.  A task goes to d only if it fits the window (estimates above: side kernels
 // are slower than the full-speed ones); otherwise it runs at full speed on s, P_{j+1} after
 // NS(u_j) and A_{j-1} before it, so that the step is never much slower than one stream.
 //
-// For the tiled chunks u_0 .. u_{T-1} (small fused chunks first, as in the one-stream
+// For the tiled units u_0 .. u_{T-1} (small fused chunks first, as in the one-stream
 // order, on s), with every task on d:
 //   s: P_0, [W_0], NS(u_0), [wait P_1], [W_1], NS(u_1), ..., NS(u_{T-1}), A_{T-1}, [join]
 //   d: [wait W_0], P_1, [wait NS(u_0)], A_0, [wait W_1], P_2, [wait NS(u_1)], A_1, ...
 // W_j marks the start of window j on s: P_{j+1} waits for it, so it never starts before
 // NS(u_{j-1}) and an A_{j-1} run on s are done; a P_{j+1} run on s after an A_{j-1} run on
-// d waits for that apply when the two chunks share a region.  Consecutive tiled chunks
-// are in different regions, so what runs side by side never touches the same workspace
-// bytes, and two regions are enough.  Events: 0 join, 1 + j W_j, 1 + T + j P_j done,
+// d waits for that apply when the two units share a region.  Consecutive units are in
+// different regions, so what runs side by side never touches the same workspace bytes,
+// and two regions are enough.  Events: 0 join, 1 + j W_j, 1 + T + j P_j done,
 // 1 + 2T + j NS(u_j) done, 1 + 3T + j A_j done.
-muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, const StepCfg& cfg, hipStream_t s) {
+muon_status step_pipelined(const muon_plan* p, const std::vector<Unit>& u, const StepCfg& cfg, hipStream_t s) {
     muon_status st;
     hipError_t e = hipSuccess;
     const float* abc = cfg.abc.data();
     const size_t T = u.size();
     hipStream_t d = (hipStream_t)p->side;
-    auto ch = [&](size_t j) -> const Chunk& { return p->chunks[(size_t)u[j]]; };
     const size_t EV_JOIN = 0, EV_W = 1, EV_P = 1 + T, EV_NS = 1 + 2 * T, EV_A = 1 + 3 * T;
 
     std::vector<int32_t> small;
@@ -457,48 +598,47 @@ muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, co
     }
 
     // placement of P_{j+1} and A_{j-1} beside NS(u_j) (pipe_place)
-    std::vector<double> win(T), tp(T), ta(T);
-    for (size_t j = 0; j < T; ++j) {
-        win[j] = est_ns_s(ch(j), cfg.steps);
-        tp[j] = est_prep_s(ch(j));
-        ta[j] = est_apply_s(ch(j));
-    }
+    std::vector<double> win(T, 0.0), tp(T, 0.0), ta(T, 0.0);
+    for (size_t j = 0; j < T; ++j)
+        for (int32_t i : u[j]) {
+            const Chunk& c = p->chunks[(size_t)i];
+            win[j] += est_ns_s(c, cfg.steps);
+            tp[j] += est_prep_s(c);
+            ta[j] += est_apply_s(c);
+        }
     std::vector<char> p_side, a_side;
     pipe_place(win, tp, ta, p_side, a_side);
 
-    const Chunk& c0 = ch(0);
-    if ((st = momentum_chunk(p, c0, cfg, s)) != MUON_OK) return st;
-    if ((st = ns_prep(p, c0, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+    if ((st = unit_momentum(p, u[0], cfg, s, false)) != MUON_OK) return st;
+    if ((st = unit_prep(p, u[0], cfg, s, false)) != MUON_OK) return st;
     for (size_t j = 0; j < T; ++j) {
-        const Chunk& cj = ch(j);
         if (j > 0 && p_side[j] && (e = wait(p, EV_P + j, s)) != hipSuccess) return hip_fail(e, "pipeline wait");
-        if (j > 0 && !a_side[j - 1] && (st = apply_chunk(p, ch(j - 1), cfg, s)) != MUON_OK) return st;
+        if (j > 0 && !a_side[j - 1] && (st = unit_apply(p, u[j - 1], cfg, s, false)) != MUON_OK) return st;
         if ((e = record(p, EV_W + j, s)) != hipSuccess) return hip_fail(e, "pipeline record");
         if (j == 0 && (e = wait(p, EV_W, d)) != hipSuccess) return hip_fail(e, "pipeline fork");
-        if ((st = ns_iterate(p, cj, abc, cfg.steps, s)) != MUON_OK) return st;
+        if ((st = unit_iterate(p, u[j], cfg, s)) != MUON_OK) return st;
         if (j + 1 < T) {
-            const Chunk& cn = ch(j + 1);
             if (p_side[j + 1]) {
                 if ((e = wait(p, EV_W + j, d)) != hipSuccess) return hip_fail(e, "pipeline wait");
-                if ((st = momentum_chunk(p, cn, cfg, d, true)) != MUON_OK) return st;
-                if ((st = ns_prep(p, cn, cfg.steps, cfg.eps, d, true)) != MUON_OK) return st;
+                if ((st = unit_momentum(p, u[j + 1], cfg, d, true)) != MUON_OK) return st;
+                if ((st = unit_prep(p, u[j + 1], cfg, d, true)) != MUON_OK) return st;
                 if ((e = record(p, EV_P + j + 1, d)) != hipSuccess) return hip_fail(e, "pipeline record");
             } else {
-                if (j > 0 && a_side[j - 1] && cn.region_off == ch(j - 1).region_off &&
+                if (j > 0 && a_side[j - 1] && same_region(p, u[j + 1], u[j - 1]) &&
                     (e = wait(p, EV_A + j - 1, s)) != hipSuccess)
                     return hip_fail(e, "pipeline wait");
-                if ((st = momentum_chunk(p, cn, cfg, s)) != MUON_OK) return st;
-                if ((st = ns_prep(p, cn, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+                if ((st = unit_momentum(p, u[j + 1], cfg, s, false)) != MUON_OK) return st;
+                if ((st = unit_prep(p, u[j + 1], cfg, s, false)) != MUON_OK) return st;
             }
         }
         if (a_side[j]) {
             if ((e = record(p, EV_NS + j, s)) != hipSuccess || (e = wait(p, EV_NS + j, d)) != hipSuccess)
                 return hip_fail(e, "pipeline record");
-            if ((st = apply_chunk(p, cj, cfg, d, true)) != MUON_OK) return st;
+            if ((st = unit_apply(p, u[j], cfg, d, true)) != MUON_OK) return st;
             if ((e = record(p, EV_A + j, d)) != hipSuccess) return hip_fail(e, "pipeline record");
         }
     }
-    if ((st = apply_chunk(p, ch(T - 1), cfg, s)) != MUON_OK) return st;
+    if ((st = unit_apply(p, u[T - 1], cfg, s, false)) != MUON_OK) return st;
     if ((e = record(p, EV_JOIN, d)) != hipSuccess || (e = wait(p, EV_JOIN, s)) != hipSuccess)
         return hip_fail(e, "pipeline join");
     return cfg.adam ? adam_run(p, cfg.adam_args, s) : MUON_OK;
@@ -506,14 +646,15 @@ muon_status step_pipelined(const muon_plan* p, const std::vector<int32_t>& u, co
 
 // Steps 1, 3 and 5 for one chunk, or for every chunk (-1) on one stream.  With distinct
 // regions every chunk's momentum runs first, then Newton–Schulz (small chunks grouped),
-// then every apply; chunks that share a region go through all three in turn.  With
-// `pipeline` (every chunk), the two-stream order above where the plan allows it.
+// then every apply; chunks that share a region go through all three in turn (the grouped
+// small chunks, which sit in one region back to back, together).  With `pipeline` (every
+// chunk), the two-stream order above where the plan allows it.
 muon_status step_chunks(const muon_plan* p, int32_t chunk, const StepCfg& cfg, hipStream_t s) {
     muon_status st;
     const int32_t nc = (int32_t)p->chunks.size();
     const float* abc = cfg.abc.data();
     if (chunk == -1 && cfg.pipeline) {
-        const std::vector<int32_t> u = pipeline_chunks(p);
+        const std::vector<Unit> u = pipeline_units(p);
         if (!u.empty()) return step_pipelined(p, u, cfg, s);
     }
     if (chunk == -1 && !p->shared_regions) {
@@ -524,9 +665,19 @@ muon_status step_chunks(const muon_plan* p, int32_t chunk, const StepCfg& cfg, h
             if ((st = apply_chunk(p, p->chunks[(size_t)i], cfg, s)) != MUON_OK) return st;
         return cfg.adam ? adam_run(p, cfg.adam_args, s) : MUON_OK;
     }
+    bool group_done = false;
     for (int32_t i = 0; i < nc; ++i) {
         if (chunk != -1 && i != chunk) continue;
         const Chunk& ch = p->chunks[(size_t)i];
+        if (chunk == -1 && ch.grouped) {
+            if (group_done) continue;
+            group_done = true;
+            const Unit g = grouped_chunks(p);
+            if ((st = unit_momentum(p, g, cfg, s, false)) != MUON_OK) return st;
+            if ((st = ns_group(p, g, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
+            if ((st = unit_apply(p, g, cfg, s, false)) != MUON_OK) return st;
+            continue;
+        }
         if ((st = momentum_chunk(p, ch, cfg, s)) != MUON_OK) return st;
         if ((st = ns_one(p, i, abc, cfg.steps, cfg.eps, s)) != MUON_OK) return st;
         if ((st = apply_chunk(p, ch, cfg, s)) != MUON_OK) return st;
@@ -967,6 +1118,8 @@ const char* muon_kernel_name(int32_t k) {
         case MUON_KERNEL_MOMENTUM_SIDE: return "momentum_side";
         case MUON_KERNEL_NORMALIZE_SIDE: return "normalize_side";
         case MUON_KERNEL_APPLY_SIDE: return "apply_side";
+        case MUON_KERNEL_NS_GROUPED: return "ns_grouped";
+        case MUON_KERNEL_PREP_GROUPED: return "prep_grouped";
         default: return "unknown";
     }
 }

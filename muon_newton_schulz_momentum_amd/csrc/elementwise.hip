@@ -251,21 +251,31 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
 // ---------------------------------------------------------------------------------------
 // Normaliser: inv = 1 / (sqrt(sum of squares) + eps) per matrix, then X = bf16(X0 * inv).
 // ---------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
-    __shared__ double red[4];
+// One matrix's normaliser 1 / (sqrt(sum of its tile partials) + eps) by a 256-thread
+// block, in a fixed order: thread i adds partials i, i + 256, ...; each wave's butterfly;
+// then the four waves pairwise.  Every thread gets the value (red: 5 doubles of LDS).
+__device__ __forceinline__ double block_inv(const double* part, int64_t ew_tiles, double eps, double* red) {
     const int tid = threadIdx.x;
-    if (blockIdx.x == 0 && tid < SCHED_WORDS) a.sched[tid] = 0u;
-    const int64_t mat = blockIdx.x;
-    const double* p = a.partials + mat * a.ew_tiles;
     double s = 0.0;
-    for (int64_t i = tid; i < a.ew_tiles; i += 256) s += p[i];
+    for (int64_t i = tid; i < ew_tiles; i += 256) s += part[i];
     s = dev::wave_sum(s);
     if ((tid & 63) == 0) red[tid >> 6] = s;
     __syncthreads();
     if (tid == 0) {
         const double tot = (red[0] + red[1]) + (red[2] + red[3]);
-        a.inv[mat] = 1.0 / (sqrt(tot) + a.eps);
+        red[4] = 1.0 / (sqrt(tot) + eps);
     }
+    __syncthreads();
+    return red[4];
+}
+
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
+    __shared__ double red[5];
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0 && tid < SCHED_WORDS) a.sched[tid] = 0u;
+    const int64_t mat = blockIdx.x;
+    const double inv = block_inv(a.partials + mat * a.ew_tiles, a.ew_tiles, a.eps, red);
+    if (tid == 0) a.inv[mat] = inv;
     if (a.x0) {
         // X0's padding: the rows past m whole, and columns n .. np-1 of the first m rows
         // (whole 16-byte units from the first multiple of 8 at or past n, single elements
@@ -957,6 +967,39 @@ hipError_t launch_momentum(const MomentumArgs& a, int32_t grad_dtype, hipStream_
         hipLaunchKernelGGL(momentum_kernel<MUON_DTYPE_F32>, dim3(grid), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(momentum_kernel<MUON_DTYPE_BF16>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// The normalisation of several small chunks in one launch (PrepGroupArgs): the
+// normaliser as finalize_kernel computes it, X = bf16(X0 * f32(inv)) per 16-byte unit as
+// normalize_kernel computes it (padding zeroed), each matrix's units split over its
+// job's `blocks` workgroups.
+__global__ __launch_bounds__(256) void prep_grouped_kernel(PrepGroupArgs g) {
+    __shared__ double red[5];
+    const int64_t blk = blockIdx.x;
+    int j = 0;
+    while (j + 1 < g.n_jobs && blk >= g.job[j + 1].first) ++j;
+    const PrepJob& J = g.job[j];
+    const int64_t local = blk - J.first;
+    const int64_t mat = local / J.blocks, part = local - mat * J.blocks;
+    const double inv = block_inv(J.partials + mat * J.ew_tiles, J.ew_tiles, g.eps, red);
+    const int64_t upr = J.np / 8, units = J.mp * upr;
+    const int64_t per = (units + J.blocks - 1) / J.blocks;
+    const int64_t u0 = part * per, u1 = units < u0 + per ? units : u0 + per;
+    const int64_t base = mat * J.mp * J.np;
+    for (int64_t u = u0 + threadIdx.x; u < u1; u += 256) {
+        const int64_t r = u / upr, c = (u - r * upr) * 8;
+        const int64_t off = base + r * J.np + c;
+        uint4 o = make_uint4(0, 0, 0, 0);
+        if (r < J.m && c < J.n) o = normalize_unit(*reinterpret_cast<const uint4*>(J.src + off), c, J.n, inv);
+        *reinterpret_cast<uint4*>(J.dst + off) = o;
+    }
+}
+
+hipError_t launch_prep_grouped(const PrepGroupArgs& g, hipStream_t s) {
+    if (g.n_jobs < 1 || g.n_jobs > PREP_MAX_JOBS || g.total_blocks < 1 || g.total_blocks >= (int64_t(1) << 31))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prep_grouped_kernel, dim3((unsigned)g.total_blocks), dim3(256), 0, s, g);
     return hipGetLastError();
 }
 

@@ -96,6 +96,42 @@ struct NsArgs {
     const double* inv;
 };
 
+// Every small tiled chunk (128- or 64-row tiles) of a plan in one launch per product: job
+// j is one chunk's NsArgs (as for launch_ns) and its first entry in the launch's tile queue.
+constexpr int GROUPED_MAX_JOBS = 12;
+
+struct GroupedJob {
+    NsArgs a;
+    int32_t tile;          // TILE_128 or TILE_64
+    int32_t first;         // queue index of the job's tile 0
+};
+
+struct GroupedNsArgs {
+    GroupedJob job[GROUPED_MAX_JOBS];
+    int32_t n_jobs;
+    int32_t total_tiles;
+};
+
+// The normalisation of small tiled chunks in one launch: per matrix, the normaliser summed
+// in the finalize kernel's order, then X = bf16(X0 * f32(inv)) as the normalize kernel does
+// it, the matrix's units spread over `blocks` workgroups (each sums the partials itself).
+constexpr int PREP_MAX_JOBS = 12;
+struct PrepJob {
+    const double* partials;
+    const uint16_t* src;   // X0
+    uint16_t* dst;         // X (may equal src)
+    int64_t ew_tiles;
+    int64_t m, n, mp, np;
+    int64_t blocks;        // workgroups per matrix
+    int64_t first;         // first workgroup of this job
+};
+struct PrepGroupArgs {
+    PrepJob job[PREP_MAX_JOBS];
+    int32_t n_jobs;
+    int64_t total_blocks;
+    double eps;
+};
+
 // Whole Newton–Schulz of small matrices (canonical m <= 64, padded n <= SMALL_NS_MAX_N,
 // see plan_internal.h),
 // one workgroup per matrix; every job is one chunk of such matrices.
@@ -131,6 +167,8 @@ hipError_t launch_normalize_side(const NormalizeArgs& a, hipStream_t s);
 hipError_t launch_apply_side(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s);
 hipError_t launch_ns_small(const SmallNsArgs& a, int64_t total, hipStream_t s);
+hipError_t launch_ns_grouped(NsMode mode, const GroupedNsArgs& g, hipStream_t s);
+hipError_t launch_prep_grouped(const PrepGroupArgs& g, hipStream_t s);
 // Zero `units` 16-byte units at `dst` (a kernel, so it may sit in a captured graph).
 hipError_t launch_zero(void* dst, uint64_t units, hipStream_t s);
 

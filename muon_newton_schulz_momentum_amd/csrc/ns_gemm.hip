@@ -165,8 +165,10 @@ __device__ __forceinline__ int kn_swz(int k) { return (k & 3) | ((k >> 1) & 4); 
 // consecutive rows, which get 8 different granules.
 __device__ __forceinline__ int ep_swz(int r) { return r & 7; }
 
+// One TILE x TILE output tile (index b of the launch's tile order) of the products on the
+// smaller tiles, with the LDS stages at `smem`; run by all 64 * WM * WN threads.
 template <int MODE, int TILE, int WM, int WN, int BK, int STAGES>
-__global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
+__device__ __forceinline__ void gemm_tile(const NsArgs& p, const int b, uint16_t (*smem)[2][TILE * BK]) {
     constexpr int NW = WM * WN;
     constexpr int WTM = TILE / WM, WTN = TILE / WN;   // wave tile
     constexpr int FM = WTM / 32, FN = WTN / 32;       // 32 x 32 MFMA blocks per wave
@@ -190,13 +192,10 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
     static_assert(STAGES >= 2 && KSUB >= 1, "pipeline");
     static_assert(TILE * TILE <= STAGES * 2 * PANEL, "epilogue tile fits in the stages");
 
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][2][PANEL];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
 
-    const int b = xcd_remap(blockIdx.x, gridDim.x);
     const int mat = b / p.tiles_per_mat;
     const int t = b - mat * p.tiles_per_mat;
     int ti, tj;
@@ -452,6 +451,35 @@ __global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
                 }
             }
         }
+    }
+}
+
+// One chunk: one tile per workgroup, tiles of a matrix kept on one XCD.
+template <int MODE, int TILE, int WM, int WN, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void ns_gemm_kernel(NsArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES][2][TILE * BK];
+    gemm_tile<MODE, TILE, WM, WN, BK, STAGES>(p, xcd_remap(blockIdx.x, gridDim.x), smem);
+}
+
+// Every small tiled chunk of a plan in one launch per product: one tile queue over the
+// jobs' tiles (job j's tiles are queue entries first_j ..), 128- and 64-row tiles alike.
+// Each workgroup takes queue entries blockIdx.x, blockIdx.x + gridDim.x, ..., and runs a
+// tile exactly as the one-chunk launch does (same code, same K order), so a matrix's result
+// does not depend on which launch computed it.
+constexpr int G_BK = 64, G_STAGES = 2;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ns_grouped_kernel(GroupedNsArgs g) {
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[G_STAGES * 2 * 128 * G_BK];
+    for (int t = blockIdx.x; t < g.total_tiles; t += gridDim.x) {
+        int j = 0;
+        while (j + 1 < g.n_jobs && t >= g.job[j + 1].first) ++j;
+        const int b = t - g.job[j].first;
+        if (g.job[j].tile == TILE_128)
+            gemm_tile<MODE, 128, 2, 2, G_BK, G_STAGES>(g.job[j].a, b, reinterpret_cast<uint16_t (*)[2][128 * G_BK]>(smem));
+        else
+            gemm_tile<MODE, 64, 2, 2, G_BK, G_STAGES>(g.job[j].a, b, reinterpret_cast<uint16_t (*)[2][64 * G_BK]>(smem));
+        __syncthreads();                                  // the tile's LDS reads are done
     }
 }
 
@@ -912,11 +940,33 @@ hipError_t launch_mode(int32_t tile, const NsArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Two workgroups per CU (64 KB of LDS each), at most one queue entry each per round.
+constexpr int GROUPED_GRID = 512;
+
+template <int MODE>
+hipError_t launch_grouped_mode(const GroupedNsArgs& g, hipStream_t s) {
+    const int grid = g.total_tiles < GROUPED_GRID ? g.total_tiles : GROUPED_GRID;
+    hipLaunchKernelGGL((ns_grouped_kernel<MODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
+    return hipGetLastError();
+}
+
 hipError_t launch_ns(NsMode mode, int32_t tile, const NsArgs& a, hipStream_t s) {
     switch (mode) {
         case NS_SYRK: return launch_mode<NS_SYRK>(tile, a, s);
         case NS_POLY: return launch_mode<NS_POLY>(tile, a, s);
         case NS_AXPY: return launch_mode<NS_AXPY>(tile, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ns_grouped(NsMode mode, const GroupedNsArgs& g, hipStream_t s) {
+    if (g.n_jobs < 1 || g.n_jobs > GROUPED_MAX_JOBS || g.total_tiles < 1) return hipErrorInvalidValue;
+    for (int j = 0; j < g.n_jobs; ++j)
+        if ((g.job[j].tile != TILE_128 && g.job[j].tile != TILE_64) || g.job[j].a.inv) return hipErrorInvalidValue;
+    switch (mode) {
+        case NS_SYRK: return launch_grouped_mode<NS_SYRK>(g, s);
+        case NS_POLY: return launch_grouped_mode<NS_POLY>(g, s);
+        case NS_AXPY: return launch_grouped_mode<NS_AXPY>(g, s);
         default: return hipErrorInvalidValue;
     }
 }

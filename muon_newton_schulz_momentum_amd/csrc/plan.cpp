@@ -79,6 +79,7 @@ void layout_region(Chunk& c, uint64_t base) {
     c.off_sched = off; off = align_up(off + SCHED_BYTES, WS_ALIGN);
     c.region_off = base;
     c.region_bytes = off - base;
+    c.region_base = base;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -171,7 +172,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     if (scale_mode != MUON_SCALE_NONE && scale_mode != MUON_SCALE_ASPECT && scale_mode != MUON_SCALE_RMS_MATCH)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown scale_mode");
     const uint32_t flags = opts ? opts->flags : 0u;
-    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_PIPELINE | MUON_PLAN_UNFUSED_NORMALIZE)) != 0)
+    if ((flags & ~(MUON_PLAN_TILED_SMALL | MUON_PLAN_PIPELINE | MUON_PLAN_UNFUSED_NORMALIZE | MUON_PLAN_UNGROUPED)) != 0)
         return set_error(MUON_ERR_INVALID_ARG, "muon_plan_buckets: unknown flag bits");
 
     // ---- validate every descriptor -----------------------------------------------------
@@ -424,6 +425,7 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
             ch.bucket = bucket_id; ch.grad_dtype = g.gdt;
             ch.m = g.m; ch.n = g.n; ch.mp = g.mp; ch.np = g.np; ch.tile = g.tile;
             ch.fused = fused;
+            ch.grouped = !fused && g.tile != TILE_256 && !(flags & MUON_PLAN_UNGROUPED);
             ch.count = cnt; ch.first = (int64_t)p->table.size(); ch.ew_tiles = g.ew;
             ch.off_table = (uint64_t)ch.first * sizeof(MatEntry);
             const int32_t cidx = (int32_t)p->chunks.size();
@@ -443,8 +445,35 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
     }
 
     // ---- workspace layout ---------------------------------------------------------------
+    // With shared regions the grouped small chunks (orthogonalised together) sit back to
+    // back in one region; if they do not fit in one under the cap, each runs on its own.
+    if (p->shared_regions) {
+        const uint64_t slack = (double_buffer ? 14 : 7) * WS_ALIGN;
+        uint64_t room = cap > p->table_bytes + slack ? cap - p->table_bytes - slack : 0;
+        if (double_buffer) room /= 2;
+        uint64_t group = 0;
+        for (Chunk& c : p->chunks)
+            if (c.grouped) {
+                layout_region(c, 0);
+                group += c.region_bytes;
+            }
+        if (group > room)
+            for (Chunk& c : p->chunks) c.grouped = false;
+    }
+    // lays the grouped chunks out back to back from `base`; returns the bytes they take
+    auto layout_group = [&](uint64_t base) {
+        uint64_t o = base;
+        for (Chunk& c : p->chunks)
+            if (c.grouped) {
+                layout_region(c, o);
+                c.region_base = base;
+                o = c.region_off + c.region_bytes;
+            }
+        return o - base;
+    };
     uint64_t off = p->table_bytes, shared_max = 0;
     for (Chunk& c : p->chunks) {
+        if (c.grouped && p->shared_regions) continue;
         if (p->shared_regions) {
             layout_region(c, p->table_bytes);
             shared_max = std::max(shared_max, c.region_bytes);
@@ -453,14 +482,25 @@ muon_status muon_plan_buckets(const muon_param_desc* params, int64_t n,
             off = c.region_off + c.region_bytes;
         }
     }
+    if (p->shared_regions) shared_max = std::max(shared_max, layout_group(p->table_bytes));
     bool second = false;
     if (double_buffer) {
         // the tiled chunks alternate between two regions (the fused small-matrix chunks,
         // which the two-stream step runs one at a time first, stay in the first), so that
-        // consecutive tiled chunks never share one
+        // consecutive tiled chunks never share one; the grouped chunks count as one
         int64_t k = 0;
+        bool group_seen = false;
         for (Chunk& c : p->chunks) {
             if (c.fused) continue;
+            if (c.grouped) {
+                if (group_seen) continue;
+                group_seen = true;
+                if (k++ & 1) {
+                    layout_group(p->table_bytes + shared_max);
+                    second = true;
+                }
+                continue;
+            }
             if (k++ & 1) {
                 layout_region(c, p->table_bytes + shared_max);
                 second = true;
@@ -506,7 +546,7 @@ muon_status muon_plan_info(const muon_plan* plan, int32_t chunk, muon_chunk_info
     out->bucket = c.bucket; out->tile = c.tile; out->grad_dtype = c.grad_dtype;
     out->shared_region = plan->shared_regions ? 1 : 0;
     out->fused_small = c.fused ? 1 : 0;
-    out->reserved = 0;
+    out->grouped_small = c.grouped ? 1 : 0;
     const double m = (double)c.m, n = (double)c.n, k = (double)c.count;
     out->flops_conventional = k * (4.0 * m * m * n + 2.0 * m * m * m);
     out->flops_algorithmic = k * (m * (m + 1.0) * n + m * m * (m + 1.0) + 2.0 * m * m * n);

@@ -35,12 +35,14 @@ struct Chunk {
     int64_t mp, np;          // padded shape: multiples of the tile
     int32_t tile;
     bool fused = false;      // the whole NS runs in the fused small-matrix kernel
+    bool grouped = false;    // a small tiled chunk: NS in the grouped launches of all such chunks
     int64_t count;           // matrices in this chunk
     int64_t first;           // first row of this chunk in the matrix table
     // elementwise tiling: 64 x 64 tiles over rows x cols (same count for both orientations)
     int64_t ew_tiles;
-    // workspace layout (byte offsets from the workspace base)
-    uint64_t region_off, region_bytes;
+    // workspace layout (byte offsets from the workspace base); region_base identifies the
+    // region the chunk's buffers live in (grouped small chunks share one, back to back)
+    uint64_t region_off, region_bytes, region_base;
     uint64_t off_xp, off_xq, off_a, off_b, off_part, off_inv;
     uint64_t off_sched;      // tile-queue counters of the persistent product kernels (zero between launches)
     uint64_t off_table;      // this chunk's first table row

@@ -558,3 +558,50 @@ def test_pipeline_plans_of_random_bucket_mixes_are_well_formed():
             for i in infos:
                 assert i["region_offset"] + i["region_bytes"] <= nbytes.value
             L.muon_plan_destroy(p)
+
+
+def test_grouped_small_chunks_layout():
+    """Small tiled chunks (128/64-row tiles, not fused) are marked for the grouped launches;
+    under a cap they sit back to back in one region (the two-stream plan: the region after
+    the last 256-tile chunk's), and when they do not fit in one region each runs alone."""
+    shapes = [(1024, 2048)] * 8 + [(512, 4096)] * 2 + [(256, 4096), (32, 4096), (4096, 1), (64, 128), (300, 700)]
+    st, p = _plan(_descs(shapes))
+    assert st == 0
+    infos = _infos(p)
+    grouped = {(i["m"], i["n"]) for i in infos if i["grouped_small"]}
+    assert grouped == {(512, 4096), (256, 4096), (32, 4096), (1, 4096), (300, 700)}
+    assert all(not i["grouped_small"] for i in infos if i["tile"] == 256 or i["fused_small"])
+    L.muon_plan_destroy(p)
+    st, p = _plan(_descs(shapes), flags=L.MUON_PLAN_UNGROUPED)
+    assert st == 0 and not any(i["grouped_small"] for i in _infos(p))
+    full = C.c_uint64()
+    L.muon_plan_workspace_bytes(p, C.byref(full))
+    L.muon_plan_destroy(p)
+    for flags in (0, L.MUON_PLAN_PIPELINE):
+        cap = full.value // 2
+        st, p = _plan(_descs(shapes), cap=cap, flags=flags)
+        assert st == 0, L.muon_last_error()
+        nb = C.c_uint64()
+        L.muon_plan_workspace_bytes(p, C.byref(nb))
+        infos = _infos(p)
+        group = [i for i in infos if i["grouped_small"]]
+        assert len(group) == 5 and all(i["shared_region"] for i in infos)
+        for a, b in zip(group, group[1:]):
+            assert b["region_offset"] == a["region_offset"] + a["region_bytes"]
+        g_lo, g_hi = group[0]["region_offset"], group[-1]["region_offset"] + group[-1]["region_bytes"]
+        assert g_hi <= nb.value
+        big = [i for i in infos if i["tile"] == 256]
+        starts = sorted({i["region_offset"] for i in big})
+        assert g_lo in starts
+        if flags:
+            assert g_lo != big[-1]["region_offset"]      # the group follows the last big chunk
+        L.muon_plan_destroy(p)
+    # a group too large for one region under the cap: every small chunk on its own
+    many = [(1024, 1024)] * 2 + [(512, 4096)] * 40 + [(256, 4096)] * 2
+    st, p = _plan(_descs(many), flags=L.MUON_PLAN_UNGROUPED)
+    L.muon_plan_workspace_bytes(p, C.byref(full))
+    L.muon_plan_destroy(p)
+    st, p = _plan(_descs(many), cap=full.value // 3)
+    assert st == 0, L.muon_last_error()
+    assert not any(i["grouped_small"] for i in _infos(p))
+    L.muon_plan_destroy(p)

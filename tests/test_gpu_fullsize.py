@@ -237,8 +237,16 @@ def test_moe_slice_full_size_two_stream_graph():
     infos = [plan.chunk_info(c) for c in range(plan.n_chunks)]
     tiled = [c for c, i in enumerate(infos) if not i.fused_small]
     assert all(infos[c].shared_region for c in tiled)
-    offs = [infos[c].region_offset for c in tiled]
+    # the 256-tile chunks alternate between two regions; the small tiled chunks (router,
+    # gates, global-layer KV) are grouped, back to back in the region after the last one
+    big = [c for c in tiled if not infos[c].grouped_small]
+    group = [c for c in tiled if infos[c].grouped_small]
+    offs = [infos[c].region_offset for c in big]
     assert len(set(offs)) == 2 and all(offs[j] != offs[j - 1] for j in range(1, len(offs)))
+    assert len(group) == 4 and group == tiled[len(big):]
+    assert infos[group[0]].region_offset in set(offs) and infos[group[0]].region_offset != offs[-1]
+    for a, b in zip(group, group[1:]):
+        assert infos[b].region_offset >= infos[a].region_offset + infos[a].region_bytes
     assert [infos[c].tile for c in tiled] == sorted((infos[c].tile for c in tiled), key=lambda t: t != 256)
     print(f"[moe_slice two-stream] {plan.n_chunks} chunks in {plan.workspace_bytes / GiB:.2f} GiB", flush=True)
     g = plan.capture_ex(w.beta, w.lr, w.wd, pipeline=True, a=w.a, b=w.b, c=w.c, steps=w.steps, eps=w.eps)

@@ -54,12 +54,18 @@ def _replay_against_eager(shapes, seed, replays, max_ws=0):
     plan = harness.Plan(graph_p, max_workspace_bytes=max_ws)
     torch.cuda.synchronize()
     g = plan.capture(BETA, LR, WD, A, B, C, K, EPS)
-    fused = sum(plan.chunk_info(c).fused_small for c in range(plan.n_chunks))
-    tiled = plan.n_chunks - fused
-    # momentum + apply per chunk; tiled chunks: finalize, normalize, 3 per iteration;
-    # fused chunks: one grouped launch (up to 8 chunks) when the chunks have their own regions
-    small_launches = fused if plan.chunk_info(0).shared_region else -(-fused // 8)
-    assert g.nodes == 2 * plan.n_chunks + tiled * (2 + 3 * K) + small_launches
+    infos = [plan.chunk_info(c) for c in range(plan.n_chunks)]
+    fused = sum(i.fused_small for i in infos)
+    grouped = sum(i.grouped_small for i in infos)
+    big = [i for i in infos if not i.fused_small and not i.grouped_small]
+    # momentum + apply per chunk; 256-tile chunks: finalize (and normalize unless the first
+    # iteration's loads normalise: odd K), 3 per iteration; small tiled chunks: one grouped
+    # normalisation and 3 grouped launches per iteration (up to 12 chunks each); fused
+    # chunks: one grouped launch (up to 8 chunks) when the chunks have their own regions
+    prep = sum(1 if (i.tile == 256 and K % 2 == 1) else 2 for i in big)
+    small_launches = fused if infos[0].shared_region else -(-fused // 8)
+    group_launches = -(-grouped // 12) * (1 + 3 * K)
+    assert g.nodes == 2 * plan.n_chunks + prep + 3 * K * len(big) + small_launches + group_launches
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed + 1)
     for r in range(replays):

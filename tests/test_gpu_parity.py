@@ -333,13 +333,25 @@ def test_kernel_timing_records_launches(mm):
     harness, _ = mm
     from muon_newton_schulz_momentum_amd import binding as L
     params = _make([(256, 512)] * 2, seed=15)
-    plan = harness.Plan(params)
+    plan = harness.Plan(params, flags=L.MUON_PLAN_UNGROUPED)
     plan.timing_enable(64)
     _run(plan, 0.95, 0.02, 0.1)
     ms, n, work = plan.timing_read(L.MUON_KERNEL_GEMM_AXPY)
     assert n == K and ms > 0 and work == pytest.approx(K * 2 * 2.0 * 256 * 256 * 512)
     ms, n, work = plan.timing_read(L.MUON_KERNEL_MOMENTUM)
     assert n == 1 and work == 2 * 256 * 512 * 14
+    plan.close()
+    # the same small chunk in the grouped launches: all three products under one kind
+    grouped = harness.Plan(_make([(256, 512)] * 2, seed=15))
+    grouped.timing_enable(64)
+    _run(grouped, 0.95, 0.02, 0.1)
+    ms, n, work = grouped.timing_read(L.MUON_KERNEL_NS_GROUPED)
+    m, nn = 256.0, 512.0
+    assert n == 3 * K and ms > 0
+    assert work == pytest.approx(K * 2 * (m * (m + 1) * nn + m * m * (m + 1) + 2 * m * m * nn))
+    assert grouped.timing_read(L.MUON_KERNEL_PREP_GROUPED)[1] == 1
+    assert grouped.timing_read(L.MUON_KERNEL_GEMM_AXPY)[1] == 0
+    grouped.close()
 
 
 def test_persistent_launches_in_a_shared_region_equal_unchunked(mm):
