@@ -516,6 +516,28 @@ __device__ __forceinline__ void lds_wait_barrier() {
 template <int N>
 using ic = std::integral_constant<int, N>;
 
+// Diagonal tiles of the symmetric products (SYRK, POLY) need only their 32 x 32 blocks on
+// or above the diagonal: 36 of 64.  The 8 waves take the tile's eight 128 x 64 regions
+// (row half r, column quarter c: region 4r + c) in an order that gives the two waves of
+// each SIMD (waves w and w + 4) 8 to 10 needed blocks between them instead of up to 16:
+//   wave      0      1      2      3      4      5      6      7
+//   region  (0,2)  (0,3)  (0,1)  (1,3)  (1,0)  (1,1)  (1,2)  (0,0)
+//   pattern FULL   FULL   B      B      NONE   NONE   A      A
+// FULL: all 8 blocks; A: blocks (i, j) with i <= j (3); B: all but (3, 0) (7); NONE: none
+// (the wave only stages operands).  The blocks below the diagonal are stored as the
+// mirror of those above it.
+constexpr uint32_t DIAG_REGION = 0x06547132u;     // nibble w: region of wave w
+constexpr int PAT_FULL = 0, PAT_A = 1, PAT_B = 2, PAT_NONE = 3;
+constexpr uint32_t DIAG_PATTERN = 0x11332200u;    // nibble w: pattern of wave w
+
+__device__ __forceinline__ constexpr bool need_block(int pat, int i, int j) {
+    return pat == PAT_FULL || (pat == PAT_A && i <= j) || (pat == PAT_B && !(i == 3 && j == 0));
+}
+// fragment read r of a sub-step (r < 4: rows 32r of the region; then the columns)
+__device__ __forceinline__ constexpr bool need_frag(int pat, int r) {
+    return pat == PAT_FULL || pat == PAT_B || (pat == PAT_A && (r < 2 || r >= 4));
+}
+
 // NORM (SYRK and AXPY of the first iteration): the X operand is read as X0 and normalised
 // in the staging registers on its way to LDS (and the AXPY's E tile as it is combined), with
 // the separate normalize pass's arithmetic, so no normalised copy of X is ever written.
@@ -567,13 +589,17 @@ void ns_vs_kernel(NsArgs p) {
     int tid = threadIdx.x;
     if (PERSIST) asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave / WN) * WTM, wn0 = (wave % WN) * WTN;
     const int mat = b / p.tiles_per_mat;
     const int t = b - mat * p.tiles_per_mat;
     int ti, tj;
     if (MODE == NS_AXPY) grid_decode(t, p.tiles_m, p.tiles_n, ti, tj);
     else tri_decode(t, p.tiles_m, ti, tj);
     const bool diag = MODE != NS_AXPY && ti == tj;
+    // The wave's 128 x 64 region of the tile: on a diagonal tile of the symmetric products
+    // from DIAG_REGION (and only its blocks on or above the diagonal are computed, see
+    // DIAG_PATTERN), elsewhere by wave index.
+    const int region = diag ? (int)((DIAG_REGION >> (4 * wave)) & 15u) : wave;
+    const int wm0 = (region / WN) * WTM, wn0 = (region % WN) * WTN;
     // the matrix's normaliser (NORM), rounded to float32 as the normalize pass rounds it
     const float s_norm = NORM ? (float)p.inv[mat] : 1.f;
 
@@ -688,8 +714,10 @@ void ns_vs_kernel(NsArgs p) {
     // The main loop is straight-line code: every condition below is a compile-time
     // constant (diagonal tile or not, last two K steps or not), so the compiler's wait
     // counts stay exact (a branch would make it wait for every outstanding load).
-    auto run = [&](auto diag_c, auto pre_c) {
+    auto run = [&](auto diag_c, auto pre_c, auto pat_c) {
         constexpr bool DG = decltype(diag_c)::value, PRE = decltype(pre_c)::value;
+        constexpr int PAT = decltype(pat_c)::value;       // DIAG_PATTERN of the wave; PAT_FULL off the diagonal
+        static_assert(DG || PAT == PAT_FULL, "patterns are for diagonal tiles");
         // prologue: K step 0 into stage 0 (already in the staging registers when PRE),
         // K step 1 into the staging registers
         if (!PRE) {
@@ -702,7 +730,8 @@ void ns_vs_kernel(NsArgs p) {
         for (int i = 0; i < NCH; ++i) { gload_a(i, 1); if (!DG) gload_b(i, 1); }
         lds_wait_barrier();
 #pragma unroll
-        for (int r = 0; r < NRD; ++r) rd(r, 0, 0, fa[0], fb[0], ftr[0]);
+        for (int r = 0; r < NRD; ++r)
+            if (need_frag(PAT, r)) rd(r, 0, 0, fa[0], fb[0], ftr[0]);
         join_tr(ftr[0], fb[0]);
 
         // One K step from stage ST.  Sub-step 1 writes operand A of K step kt + 1 from the
@@ -721,10 +750,11 @@ void ns_vs_kernel(NsArgs p) {
                 for (int f = 0; f < NMF; ++f) {
                     const int i = f / FN, j = f % FN;
                     __builtin_amdgcn_sched_barrier(0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+                    if (need_block(PAT, i, j))
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     if (STAGE && last && f == 0) lds_wait_barrier();
-                    if (f < NRD && (!last || STAGE))
+                    if (f < NRD && (!last || STAGE) && need_frag(PAT, f))
                         rd(f, last ? SN : ST, last ? 0 : kk + 1, fa[nxt], fb[nxt], ftr[nxt]);
                     if (STAGE && kk == 1 && f >= NMF - NCH) {
                         swrite_a(f - (NMF - NCH), SN);
@@ -751,12 +781,22 @@ void ns_vs_kernel(NsArgs p) {
     // separate code for prefetched tiles, so that the compiler's wait before the first
     // staging write counts the previous epilogue's stores instead of merging with the
     // fresh-load path
+    auto run_diag = [&](auto pre_c) {
+        if constexpr (MODE != NS_AXPY) {
+            switch ((DIAG_PATTERN >> (4 * wave)) & 15u) {
+                case PAT_FULL: run(std::true_type{}, pre_c, ic<PAT_FULL>{}); break;
+                case PAT_A: run(std::true_type{}, pre_c, ic<PAT_A>{}); break;
+                case PAT_B: run(std::true_type{}, pre_c, ic<PAT_B>{}); break;
+                default: run(std::true_type{}, pre_c, ic<PAT_NONE>{}); break;
+            }
+        }
+    };
     if (prefetched) {
-        if (diag) run(std::true_type{}, std::true_type{});
-        else run(std::false_type{}, std::true_type{});
+        if (diag) run_diag(std::true_type{});
+        else run(std::false_type{}, std::true_type{}, ic<PAT_FULL>{});
     } else {
-        if (diag) run(std::true_type{}, std::false_type{});
-        else run(std::false_type{}, std::false_type{});
+        if (diag) run_diag(std::false_type{});
+        else run(std::false_type{}, std::false_type{}, ic<PAT_FULL>{});
     }
     // ---- epilogue ---------------------------------------------------------------------
     // The MFMAs take the right operand first, so each 32 x 32 block is accumulated
@@ -860,19 +900,25 @@ void ns_vs_kernel(NsArgs p) {
     for (int s2 = 0; s2 < TILE * 32 / NT; ++s2) {
         const int gi = tid + NT * s2;
         const int r = gi >> 5, g = gi & 31;
+        // a diagonal tile's blocks below the diagonal were not computed: mirrored below
+        if (MODE != NS_AXPY && ti == tj && (g >> 2) < (r >> 5)) continue;
         const uint4 v = *reinterpret_cast<const uint4*>(T + r * 512 + ((g ^ (r & 31)) << 4));
         *reinterpret_cast<uint4*>(orow + (int64_t)r * p.ldo + g * 8) = v;
     }
-    // the mirrored tile (symmetric products, off the diagonal): row c of it is column c of
-    // the tile.  A transposing read over 16 lanes turns 4 tile rows x 16 columns into 16
-    // mirrored rows x 4 elements; two of them give each lane 16 bytes of one mirrored row.
-    if (MODE != NS_AXPY && ti != tj) {
+    // the mirrored tile (symmetric products): row c of it is column c of the tile.  Off the
+    // diagonal it goes to tile (tj, ti) whole; on the diagonal its blocks below the diagonal
+    // fill those of the tile itself.  A transposing read over 16 lanes turns 4 tile rows x 16
+    // columns into 16 mirrored rows x 4 elements; two of them give each lane 16 bytes of one
+    // mirrored row.
+    if (MODE != NS_AXPY) {
         uint16_t* omir = out + (int64_t)tj * TILE * p.ldo + (int64_t)ti * TILE;
         const int x = lane & 15, grp = lane >> 4;
         const int ax = x & 3, mx = x >> 2;
 #pragma unroll 2
         for (int u0 = 0; u0 < 128; u0 += NW) {            // 16 columns x 32 rows per unit
             const int u = u0 + wave;
+            // mirrored rows c0 .. c0 + 15 (block (u & 15) / 2), columns of tile rows block u / 16
+            if (ti == tj && ((u & 15) >> 1) <= (u >> 4)) continue;
             const int c0 = (u & 15) * 16, r0 = (u >> 4) * 32 + 8 * grp;
             const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(T + tb(r0 + mx, c0 + 4 * ax)));
             const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(T + tb(r0 + 4 + mx, c0 + 4 * ax)));
