@@ -237,7 +237,8 @@ MUON_API muon_status muon_plan_bind(muon_plan* plan, void* workspace, uint64_t b
 MUON_API muon_status muon_momentum_update(const muon_plan* plan, int32_t chunk, float beta, void* stream);
 
 /* Step 3.  For every matrix of `chunk`: X = bf16(X0 / (||X0||_F + eps)) (the norm summed
- * in float64, X0 times the float32-rounded reciprocal in float32), then `steps`
+ * in float64; X0 times the reciprocal, the float64 product rounded once to bf16, which
+ * float32 products reach through a per-matrix float32 scale chosen for it), then `steps`
  * quintic Newton–Schulz iterations, each
  *     A = X X^T (bf16),  B = b A + c A A (bf16),  X = a X + B X (bf16),
  * with bf16 MFMA products accumulated in float32.  A and B are symmetric; only their

@@ -25,10 +25,47 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)f32x2_to_bf16x2(f, 0.0f); }
 
-// The normalisation of one 16-byte unit of 8 bf16 values: X = bf16(X0 * s), each product
-// in float32 and rounded to bf16 by the packed conversion; elements from `valid` on (the
-// padding past the matrix's last column) are zero.  Every kernel that normalises (one
-// stream, side stream, fused small matrices) uses this, so their results agree bitwise.
+// A positive float64 value rounded to float32 "to odd": the float32 value nearest d when d
+// is one, otherwise whichever of its two float32 neighbours has an odd significand.  With
+// 24 significant bits against bfloat16's 8, rounding that value to bf16 (to nearest even)
+// is the one rounding of d to bf16.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+    const float f = (float)d;
+    const double back = (double)f;
+    if (back == d || (__float_as_uint(f) & 1u)) return f;
+    return __uint_as_float(__float_as_uint(f) + (back < d ? 1u : 0xffffffffu));
+}
+
+// The float32 scale s of a matrix's normalisation X = bf16(X0 * s) (normalize8): the float32
+// value nearest inv for which bf16(f32(m * s)) = bf16(m * inv), with m * inv rounded once
+// from its float64 product, for each of the 128 bf16 significands m in [1, 2).  Scaling by a
+// power of two changes neither rounding while the values stay normal, so with that s the
+// float32 products give every normal-range element of X as X0 * inv rounded once.  One whole
+// wave calls this with the same inv (each lane checks two significands) and gets the same s;
+// candidates are f32(inv) moved by 0, +1, -1, ..., +8, -8 units of its last place (a move of
+// more than 2 was never needed over 2 million random normalisers); if none fits, or inv is
+// not a positive float32-range number, the result is f32(inv).
+__device__ __forceinline__ float exact_scale(double inv) {
+    const float s0 = (float)inv;
+    if (!(inv > 0.0) || !(inv <= 3.4028234663852886e38)) return s0;
+    const int lane = threadIdx.x & 63;
+    const float m0 = 1.0f + (float)lane * 0.0078125f, m1 = m0 + 0.5f;
+    const uint16_t t0 = f32_to_bf16(f64_to_f32_odd((double)m0 * inv));
+    const uint16_t t1 = f32_to_bf16(f64_to_f32_odd((double)m1 * inv));
+    for (int k = 0; k <= 16; ++k) {
+        const int d = (k & 1) ? (k + 1) / 2 : -(k / 2);
+        const float s = __uint_as_float(__float_as_uint(s0) + (uint32_t)d);
+        const bool ok = f32_to_bf16(m0 * s) == t0 && f32_to_bf16(m1 * s) == t1;
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0) return s;
+    }
+    return s0;
+}
+
+// The normalisation of one 16-byte unit of 8 bf16 values: X = bf16(X0 * s) for the matrix's
+// scale s (exact_scale), each product in float32 and rounded to bf16 by the packed
+// conversion; elements from `valid` on (the padding past the matrix's last column) are zero.
+// Every kernel that normalises (one stream, side stream, grouped, fused small matrices, the
+// first product iteration's loads) uses this arithmetic, so their results agree bitwise.
 __device__ __forceinline__ uint4 normalize8(uint4 in, int32_t valid, float s) {
     const uint32_t w[4] = {in.x, in.y, in.z, in.w};
     uint32_t o[4];

@@ -249,11 +249,14 @@ __global__ __launch_bounds__(256) void momentum_kernel(MomentumArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Normaliser: inv = 1 / (sqrt(sum of squares) + eps) per matrix, then X = bf16(X0 * inv).
+// Normaliser: inv = 1 / (sqrt(sum of squares) + eps) per matrix, then X = bf16(X0 * inv)
+// (one rounding, through the matrix's float32 scale).
 // ---------------------------------------------------------------------------------------
-// One matrix's normaliser 1 / (sqrt(sum of its tile partials) + eps) by a 256-thread
-// block, in a fixed order: thread i adds partials i, i + 256, ...; each wave's butterfly;
-// then the four waves pairwise.  Every thread gets the value (red: 5 doubles of LDS).
+// One matrix's normalisation scale by a 256-thread block: inv = 1 / (sqrt(sum of its tile
+// partials) + eps), the partials summed in a fixed order (thread i adds partials i, i + 256,
+// ...; each wave's butterfly; then the four waves pairwise), and the float32 scale
+// dev::exact_scale(inv) found by the first wave.  Every thread gets the scale, as a double
+// (red: 5 doubles of LDS).
 __device__ __forceinline__ double block_inv(const double* part, int64_t ew_tiles, double eps, double* red) {
     const int tid = threadIdx.x;
     double s = 0.0;
@@ -261,9 +264,10 @@ __device__ __forceinline__ double block_inv(const double* part, int64_t ew_tiles
     s = dev::wave_sum(s);
     if ((tid & 63) == 0) red[tid >> 6] = s;
     __syncthreads();
-    if (tid == 0) {
+    if (tid < 64) {
         const double tot = (red[0] + red[1]) + (red[2] + red[3]);
-        red[4] = 1.0 / (sqrt(tot) + eps);
+        const float scale = dev::exact_scale(1.0 / (sqrt(tot) + eps));
+        if (tid == 0) red[4] = (double)scale;
     }
     __syncthreads();
     return red[4];
@@ -971,7 +975,7 @@ hipError_t launch_momentum(const MomentumArgs& a, int32_t grad_dtype, hipStream_
 }
 
 // The normalisation of several small chunks in one launch (PrepGroupArgs): the
-// normaliser as finalize_kernel computes it, X = bf16(X0 * f32(inv)) per 16-byte unit as
+// scale as finalize_kernel computes it, X = bf16(X0 * scale) per 16-byte unit as
 // normalize_kernel computes it (padding zeroed), each matrix's units split over its
 // job's `blocks` workgroups.
 __global__ __launch_bounds__(256) void prep_grouped_kernel(PrepGroupArgs g) {

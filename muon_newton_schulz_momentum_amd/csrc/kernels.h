@@ -27,7 +27,7 @@ constexpr int SCHED_WORDS = 9;
 
 struct FinalizeArgs {
     const double* partials;
-    double* inv;           // per matrix: 1 / (sqrt(sum) + eps)
+    double* inv;           // per matrix: the float32 normalisation scale of 1 / (sqrt(sum) + eps)
     int64_t ew_tiles;
     double eps;
     // the chunk's tile-queue block, zeroed here before its product launches: in a region
@@ -90,7 +90,7 @@ struct NsArgs {
     // launch's last workgroup sets them back to zero for the next)
     uint32_t* sched;
     // Normalisation fused into the first iteration's loads (256-tile SYRK and AXPY only):
-    // when set, every X operand value is read as X0 and used as bf16(X0 * f32(inv[matrix]))
+    // when set, every X operand value is read as X0 and used as bf16(X0 * (float)inv[matrix])
     // (the separate normalize pass's arithmetic); X0's padding must be zero (the finalize
     // kernel zeroes it for such chunks).
     const double* inv;
@@ -113,7 +113,7 @@ struct GroupedNsArgs {
 };
 
 // The normalisation of small tiled chunks in one launch: per matrix, the normaliser summed
-// in the finalize kernel's order, then X = bf16(X0 * f32(inv)) as the normalize kernel does
+// and searched as the finalize kernel does, then X = bf16(X0 * scale) as the normalize kernel does
 // it, the matrix's units spread over `blocks` workgroups (each sums the partials itself).
 constexpr int PREP_MAX_JOBS = 12;
 struct PrepJob {

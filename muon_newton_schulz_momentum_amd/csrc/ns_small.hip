@@ -67,16 +67,17 @@ __global__ __launch_bounds__(256) void ns_small_kernel(SmallNsArgs a) {
     // A, B element (r, c): 128-byte rows, chunk (c / 8) stored at (c / 8) ^ (r & 7)
     auto mb = [](int r, int c) { return r * 128 + ((((c >> 3) ^ (r & 7))) << 4) + (c & 7) * 2; };
 
-    // ---- the normaliser, summed as the finalize kernel sums it --------------------------
+    // ---- the normalisation scale, summed and searched as the finalize kernel does ------
     {
         double s = 0.0;
         for (int64_t i = tid; i < J.ew_tiles; i += 256) s += J.partials[mat * J.ew_tiles + i];
         s = dev::wave_sum(s);
         if (lane == 0) red[wave] = s;
         __syncthreads();
-        if (tid == 0) {
+        if (wave == 0) {
             const double tot = (red[0] + red[1]) + (red[2] + red[3]);
-            inv_s = 1.0 / (sqrt(tot) + a.eps);
+            const float scale = dev::exact_scale(1.0 / (sqrt(tot) + a.eps));
+            if (lane == 0) inv_s = (double)scale;
         }
         __syncthreads();
     }

@@ -2,7 +2,7 @@
 
 A chunk of 256-row output tiles (m >= 1024) run for an odd number of iterations never
 writes the normalised X: its first SYRK and GEMM+axpy read X0 and scale each value by the
-matrix's float32 normaliser on its way into LDS, with the separate pass's arithmetic.
+matrix's normaliser on its way into LDS, with the separate pass's arithmetic.
 
 * Bitwise equal to the separate pass (the same plan built with
   MUON_PLAN_UNFUSED_NORMALIZE): W, M and O for ragged 256-tile shapes in both
