@@ -585,9 +585,10 @@ void ns_vs_kernel(NsArgs p) {
     }
     // The thread index is made opaque to the compiler in every iteration, so that the
     // offsets derived from it are recomputed per tile instead of being hoisted out of the
-    // loop and kept live through the epilogue (which then runs out of registers).
+    // loop and kept live through the epilogue (which then runs out of registers); the
+    // axpy's per-wave epilogue needs the same in the one-tile kernel.
     int tid = threadIdx.x;
-    if (PERSIST) asm volatile("" : "+v"(tid));
+    if (PERSIST || MODE == NS_AXPY) asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
     const int mat = b / p.tiles_per_mat;
     const int t = b - mat * p.tiles_per_mat;
@@ -709,6 +710,38 @@ void ns_vs_kernel(NsArgs p) {
     static_assert(NRD <= NMF && NCH <= NMF, "issue slots");
     const int nk = p.K / BK;                              // a multiple of 4
 
+    // The axpy's epilogue works per wave on its own 128 x 64 region, in two halves of 64
+    // rows, each through an 8 KB slot of LDS: half 0 in stage 0 (free once every wave has
+    // passed the barrier of the second-to-last K step, so its E rows are fetched during
+    // the last K step), half 1 in stage 1.  Waves 0-3 use the row-panel stages, waves 4-7
+    // the K x N stages.  Slot row r (128 bytes) holds 16-byte granule g of the region's
+    // row at position g ^ ((r >> 1) & 7): the 8-byte accesses of the combine (32 rows x
+    // 8 bytes per half-wave) then touch each bank pair at most twice per 512 bytes.
+    constexpr bool WEPI = MODE == NS_AXPY;
+    static_assert(!WEPI || (WM == 2 && WN == 4 && 4 * 8192 <= RP_B && 4 * 8192 <= KN_B), "epilogue slots");
+    auto slot = [&](int h) {
+        const int base = (wave < 4) ? (h ? RP_B : 0) : (h ? OFF_B + KN_B : OFF_B);
+        return base + (wave & 3) * 8192;
+    };
+    // E rows 64h .. 64h + 63 of the wave's region into its slot h (8 direct-to-LDS loads)
+    auto e_issue = [&](int h) {
+        const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)(ti * TILE + wm0 + 64 * h) * p.ldo +
+                             (int64_t)(tj * TILE + wn0);
+        const char* sl = smem + slot(h);
+        // computed here, not hoisted into the main loop's register peak
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {                     // 8 rows (1 KB) per instruction
+            const int r = 8 * k + (ln >> 3), pos = ln & 7;
+            load_to_lds(Eg + (int64_t)r * p.ldo + (pos ^ ((r >> 1) & 7)) * 8,
+                        reinterpret_cast<const uint16_t*>(sl + k * 1024));
+        }
+    };
+    // the next tile (persistent axpy): thread 0's atomic goes out before the last two K
+    // steps and its result is published at the barrier that ends the main loop
+    int grabbed = -1;
+
     bf16x8 fa[2][FM], fb[2][FN];
     bf16x4 ftr[2][FN][2];
     // The main loop is straight-line code: every condition below is a compile-time
@@ -775,7 +808,9 @@ void ns_vs_kernel(NsArgs p) {
             kstep(ic<0>{}, yes, yes, kt);
             kstep(ic<1>{}, yes, yes, kt + 1);
         }
+        if (WEPI && PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
         kstep(ic<0>{}, yes, no, nk - 2);
+        if constexpr (WEPI) e_issue(0);
         kstep(ic<1>{}, no, no, nk - 1);
     };
     // separate code for prefetched tiles, so that the compiler's wait before the first
@@ -808,65 +843,11 @@ void ns_vs_kernel(NsArgs p) {
     // transposing reads.  The E operand (A in NS_POLY, X in NS_AXPY) comes in through the
     // same layout.
     uint16_t* out = p.out + (int64_t)mat * p.stride_o;
-    char* T = smem;
-    auto tb = [](int r, int c) { return r * 512 + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2; };
     const int er = lane & 31, ec = 4 * (lane >> 5);
-    lds_wait_barrier();                                   // every wave is done with the K stages
-    // the next tile: the atomic goes out now and its result is published to the workgroup
-    // at the barrier after the result tile is staged, so its latency hides behind the E
-    // load and the combine
-    int grabbed = -1;
-    if (PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
-    if (MODE == NS_POLY || MODE == NS_AXPY) {
-        const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
-#pragma unroll 4
-        for (int i = 0; i < 128 / NW; ++i) {              // 1 KB (two rows) per instruction
-            const int q = wave + NW * i;
-            const int r = 2 * q + (lane >> 5);
-            const int g = (lane & 31) ^ (r & 31);
-            load_to_lds(Eg + (int64_t)r * p.ldo + g * 8, reinterpret_cast<const uint16_t*>(T + q * 1024));
-        }
-        wait_vm<0, true>();
-        __syncthreads();
-    }
-    uint2 res[FM][FN][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) v[w] = acc[i][j][4 * q + w];
-                if (MODE == NS_POLY || MODE == NS_AXPY) {
-                    uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
-                    if (NORM) e = dev::normalize4(e, 8, s_norm);
-                    const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) v[w] = dev::ns_combine(p.alpha, __builtin_bit_cast(float, ew[w]), p.gamma, v[w]);
-                }
-                res[i][j][q].x = dev::f32x2_to_bf16x2(v[0], v[1]);
-                res[i][j][q].y = dev::f32x2_to_bf16x2(v[2], v[3]);
-            }
-        }
-    }
-    if (MODE == NS_POLY || MODE == NS_AXPY) lds_wait_barrier();   // E reads done before T is written
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec)) = res[i][j][q];
-    if (PERSIST && threadIdx.x == 0) next_slot = grabbed;
-    lds_wait_barrier();
-    if (PERSIST) b_next = next_slot;
-    if (PF) {
-        // The next tile's K step 0 goes out now, after the result tile is in LDS (so that it
-        // does not add to the epilogue's register peak) and ahead of this tile's stores: the
-        // vector-memory counter retires in issue order and counts stores too, so the next
-        // prologue then waits only for these loads, not for the stores to drain.
+    // The next tile's K step 0 into the staging registers, ahead of the stores still to
+    // come: the vector-memory counter retires in issue order and counts stores too, so the
+    // next prologue then waits only for these loads, not for the stores to drain.
+    auto prefetch_next = [&]() {
         // the staging registers' old contents are dead on every path from here (otherwise
         // they would stay live through the epilogue into the next iteration)
 #pragma unroll
@@ -893,7 +874,123 @@ void ns_vs_kernel(NsArgs p) {
                     sb[i] = __builtin_amdgcn_raw_buffer_load_b128(nrb, vb_rp, i * RP_ROWS * p.ldb * 2, 0);
             }
         }
+    };
+    if constexpr (WEPI) {
+        // Each wave finishes its own region without workgroup barriers: for each half, the
+        // E values at its own lanes' positions, the combine aX + BX (the iteration's B
+        // product has gamma = 1, so the product term is the accumulator itself), the
+        // results written over those same 8 bytes, then read back as whole 128-byte row
+        // pieces (8 lanes per row) and stored.  Half 1's E rows go out first, so they
+        // arrive while half 0 is combined and stored.
+        if (PERSIST && threadIdx.x == 0) next_slot = grabbed;
+        lds_wait_barrier();                               // stage 1 is free; the next tile is published
+        if (PERSIST) b_next = next_slot;
+        e_issue(1);
+        auto half = [&](auto h_c) {
+            constexpr int H = decltype(h_c)::value;
+            char* sl = smem + slot(H);
+            uint2 res[2][FN][4];
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = 32 * ii + er;
+                        const int off = r * 128 + (((4 * j + q) ^ ((r >> 1) & 7)) << 4) + 2 * ec;
+                        uint2 e = *reinterpret_cast<const uint2*>(sl + off);
+                        if (NORM) e = dev::normalize4(e, 8, s_norm);
+                        const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+                        float v[4];
+#pragma unroll
+                        for (int w = 0; w < 4; ++w)
+                            v[w] = __builtin_fmaf(p.alpha, __builtin_bit_cast(float, ew[w]), acc[2 * H + ii][j][4 * q + w]);
+                        res[ii][j][q].x = dev::f32x2_to_bf16x2(v[0], v[1]);
+                        res[ii][j][q].y = dev::f32x2_to_bf16x2(v[2], v[3]);
+                    }
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = 32 * ii + er;
+                        const int off = r * 128 + (((4 * j + q) ^ ((r >> 1) & 7)) << 4) + 2 * ec;
+                        *reinterpret_cast<uint2*>(sl + off) = res[ii][j][q];
+                    }
+            // the other lanes' results written before they are read back
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0)
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint16_t* orow = out + (int64_t)(ti * TILE + wm0 + 64 * H) * p.ldo + (int64_t)(tj * TILE + wn0);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = 8 * k + (lane >> 3), pos = lane & 7;
+                const uint4 v = *reinterpret_cast<const uint4*>(sl + r * 128 + pos * 16);
+                *reinterpret_cast<uint4*>(orow + (int64_t)r * p.ldo + (pos ^ ((r >> 1) & 7)) * 8) = v;
+            }
+        };
+        wait_vm<8, true>();                               // half 0's E rows (half 1's 8 loads may be out)
+        half(ic<0>{});
+        if (PF) prefetch_next();
+        // half 1's E rows: younger than them are half 0's 8 stores and the 8 prefetch loads
+        if (PF && b_next >= 0) wait_vm<16, true>();
+        else wait_vm<8, true>();
+        half(ic<1>{});
+    } else {
+    char* T = smem;
+    auto tb = [](int r, int c) { return r * 512 + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2; };
+    lds_wait_barrier();                                   // every wave is done with the K stages
+    // the next tile: the atomic goes out now and its result is published to the workgroup
+    // at the barrier after the result tile is staged, so its latency hides behind the E
+    // load and the combine
+    if (PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
+    if (MODE == NS_POLY) {
+        const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
+#pragma unroll 4
+        for (int i = 0; i < 128 / NW; ++i) {              // 1 KB (two rows) per instruction
+            const int q = wave + NW * i;
+            const int r = 2 * q + (lane >> 5);
+            const int g = (lane & 31) ^ (r & 31);
+            load_to_lds(Eg + (int64_t)r * p.ldo + g * 8, reinterpret_cast<const uint16_t*>(T + q * 1024));
+        }
+        wait_vm<0, true>();
+        __syncthreads();
     }
+    uint2 res[FM][FN][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[w] = acc[i][j][4 * q + w];
+                if (MODE == NS_POLY) {
+                    const uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
+                    const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) v[w] = dev::ns_combine(p.alpha, __builtin_bit_cast(float, ew[w]), p.gamma, v[w]);
+                }
+                res[i][j][q].x = dev::f32x2_to_bf16x2(v[0], v[1]);
+                res[i][j][q].y = dev::f32x2_to_bf16x2(v[2], v[3]);
+            }
+        }
+    }
+    if (MODE == NS_POLY) lds_wait_barrier();              // E reads done before T is written
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec)) = res[i][j][q];
+    if (PERSIST && threadIdx.x == 0) next_slot = grabbed;
+    lds_wait_barrier();
+    if (PERSIST) b_next = next_slot;
+    if (PF) prefetch_next();
     // the tile: 256 rows x 32 granules, whole rows per 32 lanes
     uint16_t* orow = out + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
 #pragma unroll
@@ -925,6 +1022,7 @@ void ns_vs_kernel(NsArgs p) {
             const bf16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             *reinterpret_cast<bf16x8*>(omir + (int64_t)(c0 + x) * p.ldo + r0) = v8;
         }
+    }
     }
   }
   // The launch's last workgroup to finish sets the counters back to zero for the next
