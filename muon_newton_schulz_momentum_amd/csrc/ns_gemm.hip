@@ -527,6 +527,12 @@ using ic = std::integral_constant<int, N>;
 // (the wave only stages operands).  The blocks below the diagonal are stored as the
 // mirror of those above it.
 constexpr uint32_t DIAG_REGION = 0x06547132u;     // nibble w: region of wave w
+constexpr uint32_t DIAG_REGION_WAVE = 0x36541027u;  // nibble r: the wave whose region r is
+static_assert([] {
+    for (int w = 0; w < 8; ++w)
+        if (((DIAG_REGION_WAVE >> (4 * ((DIAG_REGION >> (4 * w)) & 15u))) & 15u) != (uint32_t)w) return false;
+    return true;
+}(), "DIAG_REGION_WAVE inverts DIAG_REGION");
 constexpr int PAT_FULL = 0, PAT_A = 1, PAT_B = 2, PAT_NONE = 3;
 constexpr uint32_t DIAG_PATTERN = 0x11332200u;    // nibble w: pattern of wave w
 
@@ -586,9 +592,9 @@ void ns_vs_kernel(NsArgs p) {
     // The thread index is made opaque to the compiler in every iteration, so that the
     // offsets derived from it are recomputed per tile instead of being hoisted out of the
     // loop and kept live through the epilogue (which then runs out of registers); the
-    // axpy's per-wave epilogue needs the same in the one-tile kernel.
+    // per-wave epilogue needs the same in the one-tile kernel.
     int tid = threadIdx.x;
-    if (PERSIST || MODE == NS_AXPY) asm volatile("" : "+v"(tid));
+    asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
     const int mat = b / p.tiles_per_mat;
     const int t = b - mat * p.tiles_per_mat;
@@ -710,17 +716,17 @@ void ns_vs_kernel(NsArgs p) {
     static_assert(NRD <= NMF && NCH <= NMF, "issue slots");
     const int nk = p.K / BK;                              // a multiple of 4
 
-    // The axpy's epilogue works per wave on its own 128 x 64 region, in two halves of 64
-    // rows, each through an 8 KB slot of LDS: half 0 in stage 0 (free once every wave has
-    // passed the barrier of the second-to-last K step, so its E rows are fetched during
-    // the last K step), half 1 in stage 1.  Waves 0-3 use the row-panel stages, waves 4-7
-    // the K x N stages.  Slot row r (128 bytes) holds 16-byte granule g of the region's
-    // row at position g ^ ((r >> 1) & 7): the 8-byte accesses of the combine (32 rows x
-    // 8 bytes per half-wave) then touch each bank pair at most twice per 512 bytes.
-    constexpr bool WEPI = MODE == NS_AXPY;
-    static_assert(!WEPI || (WM == 2 && WN == 4 && 4 * 8192 <= RP_B && 4 * 8192 <= KN_B), "epilogue slots");
+    // The epilogue of the axpy and poly tiles works per wave on its own 128 x 64 region, in two halves of 64 rows, each through an
+    // 8 KB slot of LDS: half 0 in stage 0 (free once every wave has passed the barrier of
+    // the second-to-last K step, so its E rows are fetched during the last K step), half 1
+    // in stage 1.  Waves 0-3 use the row-panel stages, waves 4-7 the second operand's.
+    // Slot row r (128 bytes) holds 16-byte granule g of the region's row at position
+    // g ^ ((r >> 1) & 7): the 8-byte accesses of the combine (32 rows x 8 bytes per
+    // half-wave) then touch each bank pair at most twice per 512 bytes.
+    constexpr bool HAS_E = MODE != NS_SYRK;
+    static_assert(WM == 2 && WN == 4 && 4 * 8192 <= RP_B && 4 * 8192 <= B_STAGE, "epilogue slots");
     auto slot = [&](int h) {
-        const int base = (wave < 4) ? (h ? RP_B : 0) : (h ? OFF_B + KN_B : OFF_B);
+        const int base = (wave < 4) ? (h ? RP_B : 0) : (h ? OFF_B + B_STAGE : OFF_B);
         return base + (wave & 3) * 8192;
     };
     // E rows 64h .. 64h + 63 of the wave's region into its slot h (8 direct-to-LDS loads)
@@ -738,8 +744,8 @@ void ns_vs_kernel(NsArgs p) {
                         reinterpret_cast<const uint16_t*>(sl + k * 1024));
         }
     };
-    // the next tile (persistent axpy): thread 0's atomic goes out before the last two K
-    // steps and its result is published at the barrier that ends the main loop
+    // the next tile (persistent axpy and poly): thread 0's atomic goes out before the last
+    // two K steps and its result is published at the barrier that ends the main loop
     int grabbed = -1;
 
     bf16x8 fa[2][FM], fb[2][FN];
@@ -808,9 +814,9 @@ void ns_vs_kernel(NsArgs p) {
             kstep(ic<0>{}, yes, yes, kt);
             kstep(ic<1>{}, yes, yes, kt + 1);
         }
-        if (WEPI && PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
+        if (HAS_E && PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
         kstep(ic<0>{}, yes, no, nk - 2);
-        if constexpr (WEPI) e_issue(0);
+        if constexpr (HAS_E) e_issue(0);
         kstep(ic<1>{}, no, no, nk - 1);
     };
     // separate code for prefetched tiles, so that the compiler's wait before the first
@@ -836,12 +842,7 @@ void ns_vs_kernel(NsArgs p) {
     // ---- epilogue ---------------------------------------------------------------------
     // The MFMAs take the right operand first, so each 32 x 32 block is accumulated
     // transposed: acc[i][j][4q + w] = D[wm0 + 32i + (lane & 31)][wn0 + 32j + 8q + 4(lane >> 5) + w],
-    // four consecutive columns of one output row per lane and q.  The result tile goes
-    // through LDS (row r at r * 512 bytes, 16-byte granule G stored at granule G ^ (r & 31))
-    // and leaves in 16-byte stores: whole 512-byte rows for the tile itself and, for the
-    // mirrored tile of the symmetric products, 64-byte row pieces assembled with
-    // transposing reads.  The E operand (A in NS_POLY, X in NS_AXPY) comes in through the
-    // same layout.
+    // four consecutive columns of one output row per lane and q.
     uint16_t* out = p.out + (int64_t)mat * p.stride_o;
     const int er = lane & 31, ec = 4 * (lane >> 5);
     // The next tile's K step 0 into the staging registers, ahead of the stores still to
@@ -875,17 +876,22 @@ void ns_vs_kernel(NsArgs p) {
             }
         }
     };
-    if constexpr (WEPI) {
-        // Each wave finishes its own region without workgroup barriers: for each half, the
-        // E values at its own lanes' positions, the combine aX + BX (the iteration's B
-        // product has gamma = 1, so the product term is the accumulator itself), the
-        // results written over those same 8 bytes, then read back as whole 128-byte row
-        // pieces (8 lanes per row) and stored.  Half 1's E rows go out first, so they
-        // arrive while half 0 is combined and stored.
+    // Each wave finishes its own region without workgroup barriers: for each half, the E
+    // values at its own lanes' positions (axpy: X, poly: A), the combine (the axpy's product
+    // has gamma = 1, so its product term is the accumulator itself), the results written
+    // over those same 8 bytes, then read back as whole 128-byte row pieces (8 lanes per row)
+    // and stored; off the diagonal the poly also stores the half's mirror into tile (tj, ti),
+    // read back transposed.  Half 1's E rows go out first, so they arrive while half 0 is
+    // combined and stored.  On a diagonal poly tile only the blocks on or above the
+    // diagonal are stored from the regions; after a workgroup barrier (every wave's two
+    // slots then hold its region) the blocks below it are stored as the transposes of
+    // those above, read from the slots of the waves that computed them.
+    auto epilogue_per_wave = [&]() {
         if (PERSIST && threadIdx.x == 0) next_slot = grabbed;
         lds_wait_barrier();                               // stage 1 is free; the next tile is published
         if (PERSIST) b_next = next_slot;
-        e_issue(1);
+        if constexpr (HAS_E) e_issue(1);
+        auto soff = [](int r, int c) { return r * 128 + (((c >> 3) ^ ((r >> 1) & 7)) << 4) + (c & 7) * 2; };
         auto half = [&](auto h_c) {
             constexpr int H = decltype(h_c)::value;
             char* sl = smem + slot(H);
@@ -896,15 +902,21 @@ void ns_vs_kernel(NsArgs p) {
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const int r = 32 * ii + er;
-                        const int off = r * 128 + (((4 * j + q) ^ ((r >> 1) & 7)) << 4) + 2 * ec;
-                        uint2 e = *reinterpret_cast<const uint2*>(sl + off);
-                        if (NORM) e = dev::normalize4(e, 8, s_norm);
-                        const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+                        const int off = soff(32 * ii + er, 32 * j + 8 * q + ec);
                         float v[4];
 #pragma unroll
-                        for (int w = 0; w < 4; ++w)
-                            v[w] = __builtin_fmaf(p.alpha, __builtin_bit_cast(float, ew[w]), acc[2 * H + ii][j][4 * q + w]);
+                        for (int w = 0; w < 4; ++w) v[w] = acc[2 * H + ii][j][4 * q + w];
+                        if constexpr (HAS_E) {
+                            uint2 e = *reinterpret_cast<const uint2*>(sl + off);
+                            if (NORM) e = dev::normalize4(e, 8, s_norm);
+                            const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
+#pragma unroll
+                            for (int w = 0; w < 4; ++w) {
+                                const float ef = __builtin_bit_cast(float, ew[w]);
+                                v[w] = (MODE == NS_AXPY) ? __builtin_fmaf(p.alpha, ef, v[w])
+                                                         : dev::ns_combine(p.alpha, ef, p.gamma, v[w]);
+                            }
+                        }
                         res[ii][j][q].x = dev::f32x2_to_bf16x2(v[0], v[1]);
                         res[ii][j][q].y = dev::f32x2_to_bf16x2(v[2], v[3]);
                     }
@@ -913,11 +925,8 @@ void ns_vs_kernel(NsArgs p) {
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = 32 * ii + er;
-                        const int off = r * 128 + (((4 * j + q) ^ ((r >> 1) & 7)) << 4) + 2 * ec;
-                        *reinterpret_cast<uint2*>(sl + off) = res[ii][j][q];
-                    }
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(sl + soff(32 * ii + er, 32 * j + 8 * q + ec)) = res[ii][j][q];
             // the other lanes' results written before they are read back
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_s_waitcnt(0xc07f);           // lgkmcnt(0)
@@ -926,38 +935,84 @@ void ns_vs_kernel(NsArgs p) {
             uint16_t* orow = out + (int64_t)(ti * TILE + wm0 + 64 * H) * p.ldo + (int64_t)(tj * TILE + wn0);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int r = 8 * k + (lane >> 3), pos = lane & 7;
+                const int r = 8 * k + (lane >> 3), pos = lane & 7, g = pos ^ ((r >> 1) & 7);
                 const uint4 v = *reinterpret_cast<const uint4*>(sl + r * 128 + pos * 16);
-                *reinterpret_cast<uint4*>(orow + (int64_t)r * p.ldo + (pos ^ ((r >> 1) & 7)) * 8) = v;
+                // a diagonal tile's blocks below the diagonal were not computed
+                if (MODE == NS_POLY && diag && ((wm0 + 64 * H + r) >> 5) > ((wn0 + 8 * g) >> 5)) continue;
+                *reinterpret_cast<uint4*>(orow + (int64_t)r * p.ldo + g * 8) = v;
+            }
+            if (MODE == NS_POLY && !diag) {
+                // the mirror: row c of it is column c of the half; a transposing read over 16
+                // lanes turns 4 slot rows x 16 columns into 16 mirrored rows x 4 elements, two
+                // of them give each lane 16 bytes of one mirrored row (8 units of 16 mirrored
+                // rows x 32 slot rows)
+                uint16_t* omir = out + (int64_t)(tj * TILE + wn0) * p.ldo + (int64_t)(ti * TILE + wm0 + 64 * H);
+                const int x = lane & 15, grp = lane >> 4;
+                const int ax = x & 3, mx = x >> 2;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int c0 = (u & 3) * 16, r0 = (u >> 2) * 32 + 8 * grp;
+                    const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(sl + soff(r0 + mx, c0 + 4 * ax)));
+                    const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(sl + soff(r0 + 4 + mx, c0 + 4 * ax)));
+                    const bf16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    *reinterpret_cast<bf16x8*>(omir + (int64_t)(c0 + x) * p.ldo + r0) = v8;
+                }
             }
         };
-        wait_vm<8, true>();                               // half 0's E rows (half 1's 8 loads may be out)
+        if constexpr (HAS_E) wait_vm<8, true>();          // half 0's E rows (half 1's 8 loads may be out)
         half(ic<0>{});
         if (PF) prefetch_next();
-        // half 1's E rows: younger than them are half 0's 8 stores and the 8 prefetch loads
-        if (PF && b_next >= 0) wait_vm<16, true>();
-        else wait_vm<8, true>();
+        // half 1's E rows: younger than them are half 0's stores (8 rows, and 8 mirrored off
+        // the diagonal of the poly; on the diagonal some row stores may be skipped, so
+        // everything is waited for) and the axpy's 8 prefetch loads
+        if constexpr (MODE == NS_POLY) {
+            if (diag) wait_vm<0, true>();
+            else wait_vm<16, true>();
+        } else {
+            if (PF && b_next >= 0) wait_vm<16, true>();
+            else wait_vm<8, true>();
+        }
         half(ic<1>{});
+        if constexpr (MODE == NS_POLY) {
+            if (diag) {
+                __syncthreads();                          // every wave's slots hold its region
+                // the 28 blocks (bi, bj) below the diagonal, each as two units of 16 rows x 32
+                // columns, 7 units per wave: rows bi*32 + 16s + x of the tile, columns
+                // bj*32 + 8*grp .. + 7, read transposed from block (bj, bi) in the slot of the
+                // wave whose region holds it
+                const int x = lane & 15, grp = lane >> 4;
+                const int ax = x & 3, mx = x >> 2;
+                uint16_t* otile = out + (int64_t)(ti * TILE) * p.ldo + (int64_t)(ti * TILE);
+#pragma unroll 1
+                for (int u = wave; u < 56; u += NW) {
+                    int k = u >> 1, bi = 1;
+                    while (k >= bi) { k -= bi; ++bi; }
+                    const int bj = k, sh = u & 1;
+                    const int owner = (int)((DIAG_REGION_WAVE >> (4 * (4 * (bj >> 2) + (bi >> 1)))) & 15u);
+                    const int lr0 = (bj & 3) * 32, lc0 = (bi & 1) * 32 + 16 * sh;
+                    const int h = lr0 >> 6, sr0 = (lr0 & 63) + 8 * grp;
+                    const char* osl = smem + ((owner < 4) ? (h ? RP_B : 0) : (h ? OFF_B + B_STAGE : OFF_B)) +
+                                      (owner & 3) * 8192;
+                    const bf16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(osl + soff(sr0 + mx, lc0 + 4 * ax)));
+                    const bf16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(osl + soff(sr0 + 4 + mx, lc0 + 4 * ax)));
+                    const bf16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    *reinterpret_cast<bf16x8*>(otile + (int64_t)(bi * 32 + 16 * sh + x) * p.ldo + bj * 32 + 8 * grp) = v8;
+                }
+            }
+        }
+    };
+    if constexpr (HAS_E) {
+        epilogue_per_wave();
     } else {
+    // SYRK: the whole tile goes through LDS (row r at r * 512 bytes, 16-byte granule G stored
+    // at granule G ^ (r & 31)) between workgroup barriers and leaves in whole 512-byte rows,
+    // its mirror in 64-byte row pieces assembled with transposing reads.
     char* T = smem;
     auto tb = [](int r, int c) { return r * 512 + (((c >> 3) ^ (r & 31)) << 4) + (c & 7) * 2; };
     lds_wait_barrier();                                   // every wave is done with the K stages
     // the next tile: the atomic goes out now and its result is published to the workgroup
-    // at the barrier after the result tile is staged, so its latency hides behind the E
-    // load and the combine
+    // at the barrier after the result tile is staged
     if (PERSIST && threadIdx.x == 0) grabbed = grab_tile(p.sched, blockIdx.x % NUM_XCD, p.total_tiles);
-    if (MODE == NS_POLY) {
-        const uint16_t* Eg = p.ep + (int64_t)mat * p.stride_o + (int64_t)ti * TILE * p.ldo + (int64_t)tj * TILE;
-#pragma unroll 4
-        for (int i = 0; i < 128 / NW; ++i) {              // 1 KB (two rows) per instruction
-            const int q = wave + NW * i;
-            const int r = 2 * q + (lane >> 5);
-            const int g = (lane & 31) ^ (r & 31);
-            load_to_lds(Eg + (int64_t)r * p.ldo + g * 8, reinterpret_cast<const uint16_t*>(T + q * 1024));
-        }
-        wait_vm<0, true>();
-        __syncthreads();
-    }
     uint2 res[FM][FN][4];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -968,18 +1023,11 @@ void ns_vs_kernel(NsArgs p) {
                 float v[4];
 #pragma unroll
                 for (int w = 0; w < 4; ++w) v[w] = acc[i][j][4 * q + w];
-                if (MODE == NS_POLY) {
-                    const uint2 e = *reinterpret_cast<const uint2*>(T + tb(wm0 + 32 * i + er, wn0 + 32 * j + 8 * q + ec));
-                    const uint32_t ew[4] = {e.x << 16, e.x & 0xffff0000u, e.y << 16, e.y & 0xffff0000u};
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) v[w] = dev::ns_combine(p.alpha, __builtin_bit_cast(float, ew[w]), p.gamma, v[w]);
-                }
                 res[i][j][q].x = dev::f32x2_to_bf16x2(v[0], v[1]);
                 res[i][j][q].y = dev::f32x2_to_bf16x2(v[2], v[3]);
             }
         }
     }
-    if (MODE == NS_POLY) lds_wait_barrier();              // E reads done before T is written
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -998,7 +1046,7 @@ void ns_vs_kernel(NsArgs p) {
         const int gi = tid + NT * s2;
         const int r = gi >> 5, g = gi & 31;
         // a diagonal tile's blocks below the diagonal were not computed: mirrored below
-        if (MODE != NS_AXPY && ti == tj && (g >> 2) < (r >> 5)) continue;
+        if (ti == tj && (g >> 2) < (r >> 5)) continue;
         const uint4 v = *reinterpret_cast<const uint4*>(T + r * 512 + ((g ^ (r & 31)) << 4));
         *reinterpret_cast<uint4*>(orow + (int64_t)r * p.ldo + g * 8) = v;
     }
@@ -1007,7 +1055,7 @@ void ns_vs_kernel(NsArgs p) {
     // fill those of the tile itself.  A transposing read over 16 lanes turns 4 tile rows x 16
     // columns into 16 mirrored rows x 4 elements; two of them give each lane 16 bytes of one
     // mirrored row.
-    if (MODE != NS_AXPY) {
+    {
         uint16_t* omir = out + (int64_t)tj * TILE * p.ldo + (int64_t)ti * TILE;
         const int x = lane & 15, grp = lane >> 4;
         const int ax = x & 3, mx = x >> 2;
