@@ -60,16 +60,22 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed counter summary, if it is current."""
+    """HBM bytes per launch from the committed counter summary, if it is current, and a note
+    saying where the figure comes from or why there is none."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        why = ("its FETCH_SIZE pass ended in a crash of the profiler's host process and is not re-run; "
+               "moe_bucket's summary covers the same (1024, 4096) expert chunks") if workload == "moe_slice" \
+            else "counters were taken on moe_bucket only"
+        return None, f"no profiles/traffic_{workload}.json: {why}"
     with open(path) as fh:
         data = json.load(fh)
     if data.get("kernel_source_hash") != kernel_source_hash():
-        return None
+        return None, f"profiles/traffic_{workload}.json was taken with other kernel sources"
     k = data.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    if k is None:
+        return None, f"profiles/traffic_{workload}.json has no {kernel} entry"
+    return k.get("hbm_bytes_per_launch"), f"profiles/traffic_{workload}.json (FETCH_SIZE and WRITE_SIZE, calibrated)"
 
 
 def cpu_model() -> str:
@@ -320,10 +326,11 @@ def run_workload(key, args, steps, warmup, cpu_leg, detail):
     }
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
+    traffic, traffic_src = load_traffic(dom, w.key)
     rec["roofline"] = {
         "kernel": dom, "bound": dk["bound"], "achieved": round(dk["achieved"], 2),
         "peak": PEAK_BF16_TFLOPS if dk["bound"] == "mfma" else PEAK_HBM_GBS, "unit": dk["unit"],
-        "frac": round(dk["frac"], 4), "traffic": load_traffic(dom, w.key),
+        "frac": round(dk["frac"], 4), "traffic": traffic, "traffic_source": traffic_src,
         "work_per_launch": dk["work_per_launch"], "mean_launch_ms": dk["mean_launch_ms"],
         "measured_over": f"{steps} eager steps in the timed configuration, launched kernel by kernel right "
                          f"after the timed graph replays (HIP events on each kernel's own stream)",
