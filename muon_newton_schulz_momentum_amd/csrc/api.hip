@@ -290,7 +290,12 @@ muon_status ns_iterate(const muon_plan* p, const Chunk& c, const float* abc, int
         const float alpha[3] = {0.f, b_, a_}, gamma[3] = {1.f, c_, 1.f};
         for (int32_t k = 0; k < 3; ++k) {
             const NsMode mode = (NsMode)k;
-            const NsArgs g = ns_args(p, c, mode, cur, nxt, alpha[k], gamma[k], norm);
+            NsArgs g = ns_args(p, c, mode, cur, nxt, alpha[k], gamma[k], norm);
+            // Consecutive launches sweep the chunk's matrices in alternate directions (the
+            // first one against the momentum pass before it), so that each starts on the
+            // matrices whose data the previous launch touched last and the device caches
+            // still hold.  Results do not depend on the order.
+            g.reverse = (3 * it + k) % 2 == 0;
             TimedLaunch tl(p, kinds[k], mode_flops(c, mode), s);
             const hipError_t e = launch_ns(mode, c.tile, g, s);
             tl.done(s);

@@ -94,6 +94,9 @@ struct NsArgs {
     // (the separate normalize pass's arithmetic); X0's padding must be zero (the finalize
     // kernel zeroes it for such chunks).
     const double* inv;
+    // Nonzero: the 256-row tile kernels take the chunk's matrices in reverse order (the
+    // tiles of each matrix in the usual order); the other tile sizes ignore it.
+    int32_t reverse;
 };
 
 // Every small tiled chunk (128- or 64-row tiles) of a plan in one launch per product: job

@@ -596,8 +596,10 @@ void ns_vs_kernel(NsArgs p) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
-    const int mat = b / p.tiles_per_mat;
-    const int t = b - mat * p.tiles_per_mat;
+    // p.reverse: the chunk's matrices in the opposite order, each one's tiles in the same
+    const int mat0 = b / p.tiles_per_mat;
+    const int t = b - mat0 * p.tiles_per_mat;
+    const int mat = p.reverse ? p.total_tiles / p.tiles_per_mat - 1 - mat0 : mat0;
     int ti, tj;
     if (MODE == NS_AXPY) grid_decode(t, p.tiles_m, p.tiles_n, ti, tj);
     else tri_decode(t, p.tiles_m, ti, tj);
@@ -857,7 +859,8 @@ void ns_vs_kernel(NsArgs p) {
             sb[i] = __builtin_nondeterministic_value(sb[i]);
         }
         if (b_next >= 0) {
-            const int nmat = b_next / p.tiles_per_mat, nt = b_next - nmat * p.tiles_per_mat;
+            const int nmat0 = b_next / p.tiles_per_mat, nt = b_next - nmat0 * p.tiles_per_mat;
+            const int nmat = p.reverse ? p.total_tiles / p.tiles_per_mat - 1 - nmat0 : nmat0;
             int nti, ntj;
             if (MODE == NS_AXPY) grid_decode(nt, p.tiles_m, p.tiles_n, nti, ntj);
             else tri_decode(nt, p.tiles_m, nti, ntj);
