@@ -66,7 +66,7 @@ def load_traffic(kernel: str, workload: str):
     if not os.path.exists(path):
         why = ("its FETCH_SIZE pass ended in a crash of the profiler's host process and is not re-run; "
                "moe_bucket's summary covers the same (1024, 4096) expert chunks") if workload == "moe_slice" \
-            else "counters were taken on moe_bucket only"
+            else "no counter summary was taken for this workload"
         return None, f"no profiles/traffic_{workload}.json: {why}"
     with open(path) as fh:
         data = json.load(fh)
